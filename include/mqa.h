@@ -1,0 +1,135 @@
+/*
+ * mqa.h -- C ABI of libmqa.so: Multi-Query / Grouped-Query attention
+ * incremental decoding on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Shazeer 2019, "Fast Transformer Decoding: One Write-Head is
+ * All You Need"; the study notes' section 4 formula and the paper review's
+ * section 3 multi-query incremental pseudocode): every query head i of a
+ * sequence attends, with its own query vector, over ONE key/value head shared
+ * by all heads -- or, in the grouped generalisation (GQA essay, section 3),
+ * over the K/V head of its group g(i) = i / (h/G); G = 1 is MQA, G = h is
+ * MHA.  Each decode step appends one new K/V row per sequence to a growing
+ * cache and re-reads the whole cache once.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller.  The library allocates nothing and keeps no state beyond
+ *     a per-device cache of the compute-unit count.
+ *   - Layouts are dense and row-major; the head dimension d_h is innermost and
+ *     contiguous.  Every tensor pointer must be 16-byte aligned.
+ *   - q, o, Q, O, k_new, v_new and the cache share one element type
+ *     (mqa_dtype); accumulation is fp32 throughout.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *     is asynchronous on that stream and never synchronises, except
+ *     mqa_check_lens.
+ *   - Return value: MQA_OK (0) or a negative mqa_status.  Argument errors are
+ *     detected on the host before anything is enqueued; nothing is launched
+ *     when an error is returned.  Conditions that live in device memory
+ *     (lens values) cannot be reported without a synchronisation and are
+ *     handled as documented per call.
+ *   - Supported: d_h in {64, 128}; heads per group h/G <= 32; G divides h.
+ */
+#ifndef MQA_H
+#define MQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MQA_F32 = 0, MQA_BF16 = 1 } mqa_dtype;
+
+typedef enum {
+  MQA_OK = 0,
+  MQA_ERR_NULL = -1,      /* a required pointer is NULL                            */
+  MQA_ERR_SHAPE = -2,     /* b/n/h/G/m_cap out of range, G does not divide h, h/G>32 */
+  MQA_ERR_DHEAD = -3,     /* d_h not in {64, 128}                                  */
+  MQA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned               */
+  MQA_ERR_WORKSPACE = -5, /* workspace missing, misaligned or smaller than needed  */
+  MQA_ERR_LAUNCH = -6,    /* the HIP runtime refused a launch / query              */
+  MQA_ERR_DTYPE = -7,     /* unknown mqa_dtype                                     */
+  MQA_ERR_LENS = -8       /* mqa_check_lens: some lens[b] outside [0, m_cap]       */
+} mqa_status;
+
+/* A preallocated, growing K/V cache.  k and v each hold [b][m_cap][G][d_h]
+ * elements of `dtype`; row (b, p, g) is d_h contiguous elements.  The number
+ * of valid positions of sequence b lives in a separate device int32 lens[b]. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t b;      /* sequences                          */
+  int32_t m_cap;  /* capacity in positions per sequence */
+  int32_t G;      /* K/V heads (groups)                 */
+  int32_t d_h;    /* head dimension                     */
+  int32_t dtype;  /* mqa_dtype                          */
+} mqa_cache;
+
+/* mqa_kv_append -- the incremental concat of one new K/V row per sequence
+ * (paper review, section 3: new_K = concat(prev_K, k), new_V likewise).
+ *   k_new, v_new : device [b][G][d_h], cache dtype.
+ *   lens         : device int32 [b], read and updated in place:
+ *                  K[b, lens[b], :, :] = k_new[b]; V likewise; lens[b] += 1.
+ *   err_flag     : optional device int32; a sequence whose cache is full
+ *                  (lens[b] >= m_cap) or whose lens[b] < 0 is left untouched
+ *                  and *err_flag is set to 1 (never cleared by the library).
+ * The copy is bit-exact.  Call it BEFORE mqa_decode: the new token attends to
+ * itself, as in the pseudocode where the concat precedes the logits. */
+int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache,
+                  int32_t* lens, int32_t* err_flag, void* stream);
+
+/* Bytes of device workspace mqa_decode needs for `h` query heads over
+ * `cache` (split-K partial results plus a small schedule header).  Depends
+ * only on the shapes, never on the device or on lens.  Returns 0 when the
+ * arguments are invalid. */
+size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache);
+
+/* mqa_decode -- one decode step (study notes section 4:
+ * o_i = softmax(q_i K^T * scale) V; paper review section 3 einsums
+ * "bhk,bmk->bhm", softmax, "bhm,bmv->bhv").
+ *   q      : device [b][h][d_h].
+ *   lens   : device int32 [b]; sequence b attends over positions
+ *            [max(0, L - window), L) with L = clamp(lens[b], 0, m_cap).
+ *            Positions at or beyond L are never read.  L == 0 gives o = 0.
+ *   scale  : logit multiplier (1/sqrt(d_h) in the study notes; the paper
+ *            review's pseudocode uses 1).
+ *   window : 0 = attend over the whole cache; w > 0 = local attention over the
+ *            last w positions (study notes section 6.4: current + 31 previous
+ *            is w = 32).
+ *   o      : device [b][h][d_h], written.
+ *   workspace, ws_bytes : device scratch of >= mqa_decode_workspace_size()
+ *            bytes, 16-byte aligned; contents need no initialisation and are
+ *            clobbered.  Two calls that share a workspace must be ordered.
+ * Launches two kernels (split-K attention, then the exact combine). */
+int mqa_decode(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens,
+               float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
+               void* stream);
+
+/* mqa_prefill_causal -- causal attention over a whole prompt (study notes
+ * section 1: O = softmax(Q K^T / sqrt(d_h) + M) V with M_ij = -inf for j > i;
+ * paper review section 2.3 batched form with an additive mask).
+ *   Q, O    : device [b][n][h][d_h];  K, V : device [b][n][G][d_h].
+ *   cache   : optional; when non-NULL, K and V are also copied into
+ *             cache->k / cache->v at positions [0, n) of every sequence
+ *             (requires cache->b == b, G, d_h, dtype equal, n <= m_cap).
+ *   lens    : optional device int32 [b]; when non-NULL every lens[b] is set to n.
+ */
+int mqa_prefill_causal(const void* Q, const void* K, const void* V, int32_t b, int32_t n,
+                       int32_t h, int32_t G, int32_t d_h, int32_t dtype, float scale,
+                       const mqa_cache* cache, int32_t* lens, void* O, void* stream);
+
+/* Debug helper: synchronises `stream`, copies lens to the host and returns
+ * MQA_ERR_LENS if any lens[b] lies outside [0, m_cap], else MQA_OK. */
+int mqa_check_lens(const int32_t* lens, int32_t b, int32_t m_cap, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* mqa_strerror(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int mqa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MQA_H */

@@ -1,0 +1,73 @@
+/*
+ * mqa_oracle.h -- plain, slow, fp64 CPU oracle for Multi-Query / Grouped-Query
+ * attention decoding.  TEST INFRASTRUCTURE ONLY: nothing on the product path
+ * may include, link or call this file.  It shares no code with the HIP library.
+ *
+ * What it computes (sources: the Shazeer 2019 study notes, section 1 causal
+ * attention formula and section 4 per-head MQA formula; the paper review's
+ * section 3 incremental multi-query pseudocode and section 2.3 batched
+ * pseudocode with an additive mask; the GQA essay's section 3 grouping):
+ *
+ *   decode : o[b,i,:] = sum_j softmax_j(scale * q[b,i,:].K[b,j,g(i),:]) V[b,j,g(i),:]
+ *            over the cached positions j < L_b, with g(i) = i / (h/G)
+ *   prefill: O[b,t,i,:] = softmax over all j of (scale * Q[b,t,i,:].K[b,j,g(i),:] + M_tj)
+ *            applied to V, with M_tj = 0 for j <= t and -inf for j > t
+ *   append : the concatenation of one new K/V row per sequence onto the cache
+ *
+ * Element storage: dtype 0 = IEEE fp32, dtype 1 = bfloat16 held as raw 16-bit
+ * patterns.  Every input element is widened exactly to double; every sum is a
+ * plain fp64 sum in index order.
+ *
+ * Layouts (row-major, innermost last):
+ *   q, o          [b][h][dh]
+ *   K, V cache    [b][m_cap][G][dh]
+ *   k_new, v_new  [b][G][dh]
+ *   lens          int32 [b]
+ *   Q, O prefill  [b][n][h][dh];  K, V prefill [b][n][G][dh]
+ */
+#ifndef MQA_ORACLE_H
+#define MQA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* Concatenate one row per sequence onto the cache (the incremental concat of
+ * the paper review, section 3).  Sequences whose cache is already full
+ * (lens[b] >= m_cap) are left untouched and counted in *overflow. */
+int oracle_kv_append(int dtype, int b, int G, int dh, int m_cap,
+                     const void* k_new, const void* v_new, void* K, void* V,
+                     int32_t* lens, int32_t* overflow);
+
+/* One decode step over the cache.  L_b = clamp(lens[b], 0, m_cap).  window > 0
+ * restricts the visible positions to the last `window` ones (local attention,
+ * study notes section 6.4); window <= 0 means all of them.  An empty row
+ * (L_b == 0) yields zeros.  o is fp64 [b][h][dh]. */
+int oracle_decode(int dtype, int b, int h, int G, int dh, int m_cap,
+                  const void* q, const void* K, const void* V,
+                  const int32_t* lens, double scale, int window,
+                  double* o, int nthreads);
+
+/* The softmax weights of one decode row (b, i): w[j] for j < L_b (window
+ * applied).  Returns the number of weights written, or ORACLE_EINVAL. */
+int oracle_decode_weights(int dtype, int b, int h, int G, int dh, int m_cap,
+                          const void* q, const void* K, const void* V,
+                          const int32_t* lens, double scale, int window,
+                          int bi, int i, double* w);
+
+/* Causal prefill through the full masked row.  rows lists flattened (b, t)
+ * indices r = b*n + t to evaluate (NULL: all b*n rows, in order); O receives
+ * [nrows][h][dh] in fp64. */
+int oracle_prefill(int dtype, int b, int n, int h, int G, int dh,
+                   const void* Q, const void* K, const void* V, double scale,
+                   const int64_t* rows, int64_t nrows, double* O, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

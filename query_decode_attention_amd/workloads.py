@@ -1,0 +1,145 @@
+"""Seeded synthetic workloads for MQA/GQA decoding and causal prefill.
+
+This module only draws random inputs and names shapes.  It holds none of the
+method's arithmetic, so both the HIP path and the CPU oracle can be fed from
+it without sharing any computation.
+
+Recipe (identical for every consumer):
+  * generator: ``torch.Generator('cpu').manual_seed(seed)``; one call per
+    tensor in the fixed draw order q, K, V, k_new, v_new, lens (prefill: Q, K, V);
+  * values: fp32 N(0, 1), rounded to bfloat16 by round-to-nearest-even
+    (``Tensor.to(torch.bfloat16)``) for bf16 workloads;
+  * lens: uniform integers in the configured range, or a constant.
+
+The shapes stand in for the paper's workload (a WMT14 encoder-decoder on
+TPUv2, batch 1024, length 128: study notes section 6.2), which needs data and
+trained weights that are not used here; only the attention core's shapes and
+value distributions matter to it.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    dtype: torch.dtype
+    b: int
+    h: int
+    G: int
+    dh: int
+    m_cap: int
+    lens_lo: int          # pre-append lens drawn uniformly from [lens_lo, lens_hi]
+    lens_hi: int
+    append: bool          # one kv_append per sequence before the decode
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dh)
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    dtype: torch.dtype
+    b: int
+    n: int
+    h: int
+    G: int
+    dh: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dh)
+
+
+# The five workloads (shapes of the pages' problem statement, enlarged to
+# serving sizes).  Seeds are 1000 + workload number.
+C1 = DecodeConfig("c1_tiny_fp32", torch.float32, b=1, h=4, G=1, dh=64, m_cap=128,
+                  lens_lo=128, lens_hi=128, append=False, seed=1001)
+C2 = DecodeConfig("c2_mqa_b8_m2048", torch.bfloat16, b=8, h=32, G=1, dh=128, m_cap=2048,
+                  lens_lo=2048, lens_hi=2048, append=False, seed=1002)
+C2_MHA = DecodeConfig("c2_mha_b8_m2048", torch.bfloat16, b=8, h=32, G=32, dh=128,
+                      m_cap=2048, lens_lo=2048, lens_hi=2048, append=False, seed=1012)
+C3 = DecodeConfig("c3_serving_b64_ragged8k", torch.bfloat16, b=64, h=32, G=1, dh=128,
+                  m_cap=8192 + 256, lens_lo=1, lens_hi=8192, append=True, seed=1003)
+C4 = DecodeConfig("c4_gqa_b32_h64_g8_m32k", torch.bfloat16, b=32, h=64, G=8, dh=128,
+                  m_cap=32768, lens_lo=32768, lens_hi=32768, append=False, seed=1004)
+C5 = PrefillConfig("c5_prefill_b4_n4096", torch.bfloat16, b=4, n=4096, h=32, G=1, dh=128,
+                   seed=1005)
+
+DECODE_CONFIGS = {c.name: c for c in (C1, C2, C2_MHA, C3, C4)}
+PREFILL_CONFIGS = {C5.name: C5}
+
+
+def _normal(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    return x.to(dtype) if dtype != torch.float32 else x
+
+
+def _normal_chunked(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    """Same draw as ``_normal`` (one contiguous stream of N(0,1)), produced in
+    slices along dim 0 to bound host memory for multi-GB caches."""
+    if dtype == torch.float32 or shape[0] <= 1:
+        return _normal(g, shape, dtype)
+    out = torch.empty(*shape, dtype=dtype)
+    for i in range(shape[0]):
+        out[i] = torch.randn(*shape[1:], generator=g, dtype=torch.float32).to(dtype)
+    return out
+
+
+def decode_inputs(cfg: DecodeConfig, seed: Optional[int] = None, b: Optional[int] = None,
+                  m_cap: Optional[int] = None, lens_lo: Optional[int] = None,
+                  lens_hi: Optional[int] = None):
+    """CPU tensors for one decode step of ``cfg`` (optionally resized).
+
+    Returns a dict with q [b,h,dh], K,V [b,m_cap,G,dh], k_new,v_new [b,G,dh]
+    and lens int32 [b] (pre-append when cfg.append).
+    """
+    b = cfg.b if b is None else b
+    m_cap = cfg.m_cap if m_cap is None else m_cap
+    lo = cfg.lens_lo if lens_lo is None else lens_lo
+    hi = cfg.lens_hi if lens_hi is None else lens_hi
+    g = torch.Generator("cpu").manual_seed(cfg.seed if seed is None else seed)
+    q = _normal(g, (b, cfg.h, cfg.dh), cfg.dtype)
+    K = _normal_chunked(g, (b, m_cap, cfg.G, cfg.dh), cfg.dtype)
+    V = _normal_chunked(g, (b, m_cap, cfg.G, cfg.dh), cfg.dtype)
+    k_new = _normal(g, (b, cfg.G, cfg.dh), cfg.dtype)
+    v_new = _normal(g, (b, cfg.G, cfg.dh), cfg.dtype)
+    lens = torch.randint(lo, hi + 1, (b,), generator=g, dtype=torch.int64).to(torch.int32)
+    return dict(q=q, K=K, V=V, k_new=k_new, v_new=v_new, lens=lens)
+
+
+def prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None, b: Optional[int] = None,
+                   n: Optional[int] = None):
+    """CPU tensors Q [b,n,h,dh], K,V [b,n,G,dh] for a causal prefill."""
+    b = cfg.b if b is None else b
+    n = cfg.n if n is None else n
+    g = torch.Generator("cpu").manual_seed(cfg.seed if seed is None else seed)
+    Q = _normal_chunked(g, (b, n, cfg.h, cfg.dh), cfg.dtype)
+    K = _normal_chunked(g, (b, n, cfg.G, cfg.dh), cfg.dtype)
+    V = _normal_chunked(g, (b, n, cfg.G, cfg.dh), cfg.dtype)
+    return dict(Q=Q, K=K, V=V)
+
+
+def poison_beyond(cache: torch.Tensor, lens: torch.Tensor, values=(float("nan"),
+                  float("inf"), float("-inf"))) -> torch.Tensor:
+    """Copy of ``cache`` [b,m_cap,G,dh] with every position >= lens[b] set to a
+    cycling pattern of non-finite values (used to show they are never read)."""
+    out = cache.clone()
+    b, m_cap = cache.shape[:2]
+    pat = torch.tensor(values, dtype=torch.float32).to(cache.dtype)
+    for bi in range(b):
+        L = int(lens[bi])
+        if L < m_cap:
+            tail = out[bi, L:]
+            idx = torch.arange(tail.numel()) % pat.numel()
+            out[bi, L:] = pat[idx].reshape(tail.shape)
+    return out
