@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""MQA incremental decode on one MI355X: steps/s and effective KV GB/s.
+
+Headline workload: batched serving decode, b=64 sequences, h=32 query heads
+sharing G=1 K/V head, d_h=128, bf16 cache, pre-append lengths uniform in
+[1, 8192], one kv_append per sequence, then the decode (split-K attention +
+combine).  One step = append + decode for the whole batch.
+
+Timing discipline:
+  * R independently drawn caches are rotated step by step so every pass
+    touches >= 1 GiB (several times the 256 MB Infinity Cache) and the K/V
+    stream really comes from HBM;
+  * W untimed warm-up steps; then K timed steps between two
+    torch.cuda.synchronize() calls; steps are replayed from a HIP graph of R
+    steps so host launch overhead stays out of the GPU timeline;
+  * bytes per step are counted from the actual lens of each timed step.
+
+The JSON line adds
+  * roofline: the split-K attention kernel (the dominant kernel), timed with
+    HIP events recorded on its own stream around each launch;
+  * cpu_baseline: the fp64 oracle on the host cores, on a bounded sample;
+  * extra: the other workloads (MQA/MHA comparison point, GQA long context,
+    causal prefill), each with its own rotation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
+METRIC = "MQA decode steps/s + effective KV GB/s (%HBM peak), b=64 h=32 d=128 m=8K"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- decode
+
+
+class DecodeBench:
+    """R rotated copies of one decode workload living in HBM."""
+
+    def __init__(self, cfg, R, torch, mqa, seed_base=0):
+        self.cfg, self.R, self.torch = cfg, R, torch
+        dev = torch.device("cuda")
+        b, h, G, dh, m_cap = cfg.b, cfg.h, cfg.G, cfg.dh, cfg.m_cap
+        self.copies = []
+        self.lens_host = []
+        for r in range(R):
+            gg = torch.Generator(device=dev).manual_seed(cfg.seed * 1000 + seed_base + r)
+            gc = torch.Generator().manual_seed(cfg.seed * 1000 + seed_base + r)
+            K = torch.randn(b, m_cap, G, dh, generator=gg, device=dev).to(cfg.dtype)
+            V = torch.randn(b, m_cap, G, dh, generator=gg, device=dev).to(cfg.dtype)
+            q = torch.randn(b, h, dh, generator=gg, device=dev).to(cfg.dtype)
+            kn = torch.randn(b, G, dh, generator=gg, device=dev).to(cfg.dtype)
+            vn = torch.randn(b, G, dh, generator=gg, device=dev).to(cfg.dtype)
+            lens_cpu = torch.randint(cfg.lens_lo, cfg.lens_hi + 1, (b,), generator=gc,
+                                     dtype=torch.int64).to(torch.int32)
+            lens = lens_cpu.to(dev)
+            self.copies.append(dict(K=K, V=V, q=q, kn=kn, vn=vn, lens=lens))
+            self.lens_host.append(lens_cpu.tolist())
+        self.out = torch.empty(b, h, dh, dtype=cfg.dtype, device=dev)
+        self.ws = mqa.workspace_for(h, self.copies[0]["K"])
+        self.steps = []
+        for c in self.copies:
+            kw = dict(k_new=c["kn"], v_new=c["vn"]) if cfg.append else {}
+            self.steps.append(mqa.DecodeStep(c["q"], c["K"], c["V"], c["lens"], cfg.scale,
+                                             out=self.out, workspace=self.ws, **kw))
+        self.appends = [0] * R   # appends issued per copy so far
+        self.elem = 2 if cfg.dtype == torch.bfloat16 else 4
+
+    # effective (algorithmic) bytes of one step of copy r given its current appends
+    def kv_bytes(self, r, extra_appends=0):
+        cfg = self.cfg
+        n_app = self.appends[r] + extra_appends
+        tot = 0
+        for L0 in self.lens_host[r]:
+            L = min(L0 + (n_app if cfg.append else 0), cfg.m_cap)
+            tot += L
+        return tot * cfg.G * cfg.dh * 2 * self.elem
+
+    def other_bytes(self):
+        """q in, o out, lens; plus for an appending step the new rows read and written."""
+        cfg = self.cfg
+        b = 2 * cfg.b * cfg.h * cfg.dh * self.elem + 4 * cfg.b
+        if cfg.append:
+            b += 2 * 2 * cfg.b * cfg.G * cfg.dh * self.elem + 4 * cfg.b
+        return b
+
+    def flops(self, r, extra_appends=0):
+        cfg = self.cfg
+        return 4 * cfg.h * cfg.dh * self.kv_bytes(r, extra_appends) // (cfg.G * cfg.dh * 2 * self.elem)
+
+    def eager(self, n, events=None):
+        for i in range(n):
+            r = i % self.R
+            self.appends[r] += 1 if self.cfg.append else 0
+            self.steps[r](None if events is None else events[i])
+
+    def capture(self):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for r in range(self.R):
+                    self.steps[r]()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(self, steps, use_graph):
+        """Returns (seconds, total effective KV bytes, total bytes, flops, steps run)."""
+        torch = self.torch
+        R = self.R
+        graph = self.capture() if use_graph else None
+        n_rep = max(1, math.ceil(steps / R)) if use_graph else None
+        n_steps = n_rep * R if use_graph else steps
+        kv = tot = fl = 0
+        for i in range(n_steps):
+            r = i % R
+            kv += self.kv_bytes(r, 1 + i // R)
+            fl += self.flops(r, 1 + i // R)
+        tot = kv + n_steps * self.other_bytes()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if use_graph:
+            for _ in range(n_rep):
+                graph.replay()
+        else:
+            self.eager(n_steps)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if use_graph:
+            for r in range(R):
+                self.appends[r] += n_rep if self.cfg.append else 0
+        return dt, kv, tot, fl, n_steps
+
+    def kernel_timing(self, n):
+        """Average split-K kernel duration (HIP events on the launch stream) and its
+        algorithmic bytes per launch, over n eager steps queued behind a GPU sleep
+        so that launches never wait for the host."""
+        torch = self.torch
+        evs = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))      # ~20 ms of GPU spin: launches queue up
+        kv = 0
+        other = 2 * self.cfg.b * self.cfg.h * self.cfg.dh * self.elem + 4 * self.cfg.b
+        for i in range(n):
+            r = i % self.R
+            self.appends[r] += 1 if self.cfg.append else 0
+            kv += self.kv_bytes(r)
+            self.steps[r](evs[i])
+        torch.cuda.synchronize()
+        dur = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+        return sum(dur) / n, (kv + n * other) / n, kv / n
+
+
+def decode_result(bench, steps, warmup, use_graph):
+    bench.eager(warmup)
+    bench.torch.cuda.synchronize()
+    dt, kv, tot, fl, n = bench.timed(steps, use_graph)
+    return dict(seconds=dt, steps=n, steps_per_s=n / dt, ms_per_step=1e3 * dt / n,
+                kv_gbps=kv / dt / 1e9, total_gbps=tot / dt / 1e9,
+                kv_frac_of_peak=kv / dt / 1e9 / HBM_PEAK_GBPS, tflops=fl / dt / 1e12,
+                kv_bytes_per_step=kv / n)
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+def prefill_result(cfg, steps, torch, mqa, R=2):
+    dev = torch.device("cuda")
+    copies = []
+    for r in range(R):
+        g = torch.Generator(device=dev).manual_seed(cfg.seed * 1000 + r)
+        Q = torch.randn(cfg.b, cfg.n, cfg.h, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        K = torch.randn(cfg.b, cfg.n, cfg.G, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        V = torch.randn(cfg.b, cfg.n, cfg.G, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        copies.append((Q, K, V))
+    O = torch.empty_like(copies[0][0])
+    cK = torch.empty(cfg.b, cfg.n, cfg.G, cfg.dh, dtype=cfg.dtype, device=dev)
+    cV = torch.empty_like(cK)
+    lens = torch.zeros(cfg.b, dtype=torch.int32, device=dev)
+    for i in range(3):
+        Q, K, V = copies[i % R]
+        mqa.prefill_causal(Q, K, V, cfg.scale, cache_K=cK, cache_V=cV, lens=lens, out=O)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        Q, K, V = copies[i % R]
+        mqa.prefill_causal(Q, K, V, cfg.scale, cache_K=cK, cache_V=cV, lens=lens, out=O)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) * 1e-3 / steps
+    pairs = cfg.n * (cfg.n + 1) // 2
+    flops = 4 * cfg.b * cfg.h * cfg.dh * pairs
+    return dict(ms_per_call=dt * 1e3, tflops=flops / dt / 1e12,
+                mfma_frac_of_peak=flops / dt / 1e12 / BF16_PEAK_TFLOPS,
+                causal_flops=flops)
+
+
+# --------------------------------------------------------------------------- cpu baseline
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (fp64 C, threads over rows) on the host: full serving steps
+    (append + decode, all 64 sequences) repeated until ~budget_s."""
+    import numpy as np
+    import oracle
+    from query_decode_attention_amd import workloads as W
+    cfg = W.C3
+    inp = W.decode_inputs(cfg)
+    Kr, _ = oracle._raw(inp["K"])
+    Vr, _ = oracle._raw(inp["V"])
+    Kr, Vr = Kr.copy(), Vr.copy()
+    lens = inp["lens"].numpy().copy()
+    threads = oracle.default_threads()
+    n = 0
+    kv = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.kv_append(inp["k_new"], inp["v_new"], Kr, Vr, lens)
+        oracle.decode(inp["q"], Kr, Vr, lens, cfg.scale, nthreads=threads)
+        n += 1
+        kv += int(np.minimum(lens, cfg.m_cap).sum()) * cfg.G * cfg.dh * 2 * 2
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
+                sample=f"{n} full serving steps (append + decode, b=64, h=32, d_h=128, "
+                       f"ragged lens 1..8192) in {dt:.1f} s; fp64 C oracle with {threads} "
+                       f"threads over (sequence, head) rows",
+                kv_gbps=kv / dt / 1e9, seconds=dt)
+
+
+# --------------------------------------------------------------------------- main
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--rotate", type=int, default=8, help="cache copies for the headline")
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly (no HIP graph)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--kernel-steps", type=int, default=64)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: the decode path is built and measured on a "
+                  "single MI355X (multi-GPU sharding is a design note, not a run). "
+                  f"Refusing --gpus {args.gpus}.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import query_decode_attention_amd as mqa
+    from query_decode_attention_amd import workloads as W
+    mqa.load()
+    torch.cuda.set_device(0)
+    use_graph = not args.eager
+
+    log("headline: serving decode c3 (b=64, h=32, G=1, d_h=128, lens U[1,8192] + append)")
+    head = DecodeBench(W.C3, args.rotate, torch, mqa)
+    res = decode_result(head, args.steps, args.warmup, use_graph)
+    log(f"headline {res['steps_per_s']:.1f} steps/s, {res['kv_gbps']:.1f} GB/s KV "
+        f"({100 * res['kv_frac_of_peak']:.1f}% of 8 TB/s)")
+    kdur, kbytes, kkv = head.kernel_timing(args.kernel_steps)
+    achieved = kbytes / kdur / 1e9
+    log(f"split kernel avg {kdur * 1e6:.2f} us, {achieved:.1f} GB/s")
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    kernel="decode_split_kernel<bf16,128,8>",
+                    avg_launch_us=round(kdur * 1e6, 3),
+                    algorithmic_bytes_per_launch=int(kbytes))
+    del head
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        log("c2 MQA vs MHA comparison point")
+        c2 = decode_result(DecodeBench(W.C2, 64, torch, mqa), 640, 64, use_graph)
+        torch.cuda.empty_cache()
+        c2m = decode_result(DecodeBench(W.C2_MHA, 4, torch, mqa), 200, 8, use_graph)
+        torch.cuda.empty_cache()
+        extra["c2_mqa_b8_m2048"] = {k: round(v, 4) for k, v in c2.items()}
+        extra["c2_mha_b8_m2048"] = {k: round(v, 4) for k, v in c2m.items()}
+        extra["mha_over_mqa_time_ratio"] = round(c2m["ms_per_step"] / c2["ms_per_step"], 2)
+        log(f"MHA/MQA time ratio {extra['mha_over_mqa_time_ratio']}")
+        log("c4 GQA long context")
+        c4 = decode_result(DecodeBench(W.C4, 1, torch, mqa), 30, 3, use_graph)
+        torch.cuda.empty_cache()
+        extra["c4_gqa_b32_h64_g8_m32k"] = {k: round(v, 4) for k, v in c4.items()}
+        log("c5 causal prefill")
+        extra["c5_prefill_b4_n4096"] = {k: round(v, 4) if isinstance(v, float) else v
+                                        for k, v in prefill_result(W.C5, 10, torch, mqa).items()}
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)")
+        cpu = cpu_baseline()
+        cpu = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cpu.items()}
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "serving MQA decode: append + split-K decode + combine",
+                   "b": 64, "h": 32, "G": 1, "d_h": 128, "lens": "uniform [1,8192] + 1 append",
+                   "m_cap": W.C3.m_cap, "rotated_caches": args.rotate,
+                   "launch": "eager" if args.eager else "hip-graph"},
+        "kv_gbps": round(res["kv_gbps"], 1),
+        "kv_frac_of_hbm_peak": round(res["kv_frac_of_peak"], 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

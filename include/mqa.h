@@ -106,6 +106,16 @@ int mqa_decode(const void* q, int32_t h, const mqa_cache* cache, const int32_t* 
                float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
                void* stream);
 
+/* mqa_decode_timed -- mqa_decode plus kernel-level timing: the optional
+ * hipEvent_t handles ev_begin / ev_end (NULL = skip) are recorded on `stream`
+ * immediately before and after the split-K attention kernel, the step's
+ * dominant kernel, so a caller can time it with hipEventElapsedTime.  The
+ * events must have been created for `stream`'s device.  Results are identical
+ * to mqa_decode. */
+int mqa_decode_timed(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens,
+                     float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
+                     void* stream, void* ev_begin, void* ev_end);
+
 /* mqa_prefill_causal -- causal attention over a whole prompt (study notes
  * section 1: O = softmax(Q K^T / sqrt(d_h) + M) V with M_ij = -inf for j > i;
  * paper review section 2.3 batched form with an additive mask).

@@ -1,0 +1,308 @@
+"""query_decode_attention_amd -- MQA/GQA incremental decoding on MI355X (gfx950).
+
+Thin ctypes binding over ``libmqa.so`` (C ABI in ``include/mqa.h``).  This
+module only marshals arguments: it checks tensor placement, dtype, shape and
+contiguity, then passes raw device pointers and the current HIP stream of
+PyTorch.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: the first call (or ``load()``) raises ImportError if
+the library is missing.  PyTorch supplies device memory and streams only.
+
+Entry points (same names as the C ABI, minus the ``mqa_`` prefix):
+  kv_append(k_new, v_new, K, V, lens, err_flag=None)
+  decode_workspace_size(h, K)
+  decode(q, K, V, lens, scale, window=0, out=None, workspace=None)
+  prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None)
+  check_lens(lens, m_cap)
+  strerror(status)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import workloads  # noqa: F401  (seeded inputs; no arithmetic)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmqa.so")
+
+MQA_F32, MQA_BF16 = 0, 1
+_DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
+
+
+class MQAError(RuntimeError):
+    """A libmqa call returned a non-zero mqa_status."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("b", ctypes.c_int32),
+                ("m_cap", ctypes.c_int32), ("G", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m query_decode_attention_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    CP = ctypes.POINTER(_Cache)
+    lib.mqa_kv_append.argtypes = [P, P, CP, P, P, P]
+    lib.mqa_kv_append.restype = ctypes.c_int
+    lib.mqa_decode_workspace_size.argtypes = [I32, CP]
+    lib.mqa_decode_workspace_size.restype = SZ
+    lib.mqa_decode.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P]
+    lib.mqa_decode.restype = ctypes.c_int
+    lib.mqa_decode_timed.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P, P, P]
+    lib.mqa_decode_timed.restype = ctypes.c_int
+    lib.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
+    lib.mqa_prefill_causal.restype = ctypes.c_int
+    lib.mqa_check_lens.argtypes = [P, I32, I32, P]
+    lib.mqa_check_lens.restype = ctypes.c_int
+    lib.mqa_strerror.argtypes = [ctypes.c_int]
+    lib.mqa_strerror.restype = ctypes.c_char_p
+    lib.mqa_abi_version.argtypes = []
+    lib.mqa_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_lib_handle = None
+
+
+def load():
+    """Load libmqa.so (once); raises ImportError when it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
+
+
+class _LazyLib:
+    def __getattr__(self, name):
+        return getattr(load(), name)
+
+
+_lib = _LazyLib()
+
+# Symbols include/mqa.h declares (tests check the library exports each one).
+EXPORTED = ("mqa_kv_append", "mqa_decode_workspace_size", "mqa_decode", "mqa_decode_timed",
+            "mqa_prefill_causal", "mqa_check_lens", "mqa_strerror", "mqa_abi_version")
+
+
+def lib():
+    return load()
+
+
+def strerror(status: int) -> str:
+    return _lib.mqa_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return _lib.mqa_abi_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MQAError(fn, status)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("libmqa takes CUDA (HIP) tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libmqa takes contiguous tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must live on one device")
+    return dev
+
+
+def _cache(K, V):
+    if K.dim() != 4 or V.shape != K.shape or V.dtype != K.dtype:
+        raise ValueError("K and V caches must both be [b, m_cap, G, d_h] of one dtype")
+    if K.dtype not in _DTYPES:
+        raise ValueError(f"unsupported cache dtype {K.dtype}")
+    b, m_cap, G, dh = K.shape
+    return _Cache(K.data_ptr(), V.data_ptr(), b, m_cap, G, dh, _DTYPES[K.dtype])
+
+
+def kv_append(k_new, v_new, K, V, lens, err_flag=None):
+    """K[b, lens[b]] = k_new[b]; V likewise; lens[b] += 1 (in place, async)."""
+    dev = _dev(k_new, v_new, K, V, lens, err_flag)
+    b, _, G, dh = K.shape
+    if k_new.shape != (b, G, dh) or v_new.shape != (b, G, dh):
+        raise ValueError("k_new / v_new must be [b, G, d_h]")
+    if k_new.dtype != K.dtype or v_new.dtype != K.dtype:
+        raise ValueError("k_new / v_new must have the cache dtype")
+    if lens.dtype != torch.int32 or lens.shape != (b,):
+        raise ValueError("lens must be int32 [b]")
+    if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1):
+        raise ValueError("err_flag must be an int32 tensor")
+    c = _cache(K, V)
+    _check("mqa_kv_append", _lib.mqa_kv_append(_ptr(k_new), _ptr(v_new), ctypes.byref(c),
+                                                 _ptr(lens), _ptr(err_flag), _stream(K)))
+
+
+def _shape_only(K):
+    b, m_cap, G, dh = K.shape
+    return _Cache(None, None, b, m_cap, G, dh, _DTYPES.get(K.dtype, -1))
+
+
+def decode_workspace_size(h: int, K) -> int:
+    n = _lib.mqa_decode_workspace_size(int(h), ctypes.byref(_shape_only(K)))
+    if n == 0:
+        raise ValueError("invalid decode shapes")
+    return int(n)
+
+
+def workspace_for(h: int, K):
+    """Allocate a decode workspace (uint8 device tensor) for these shapes."""
+    return torch.empty(decode_workspace_size(h, K), dtype=torch.uint8, device=K.device)
+
+
+def decode(q, K, V, lens, scale, window=0, out=None, workspace=None, events=None):
+    """One decode step: o[b,i] = softmax(scale * q[b,i] . K[b,:L,g(i)]) V[b,:L,g(i)].
+
+    events: optional (begin, end) torch.cuda.Event pair, already created on
+    q's device, recorded around the split-K attention kernel.
+    """
+    if workspace is None:
+        n = _lib.mqa_decode_workspace_size(int(q.shape[1]), ctypes.byref(_shape_only(K)))
+        # invalid shapes give n == 0: the C call below then reports the exact status
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=K.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, K, V, lens, out, workspace)
+    b, m_cap, G, dh = K.shape
+    if q.dim() != 3 or q.shape[0] != b or q.shape[2] != dh:
+        raise ValueError("q must be [b, h, d_h] matching the cache")
+    if q.dtype != K.dtype or out.dtype != K.dtype or out.shape != q.shape:
+        raise ValueError("q / out must match the cache dtype and q's shape")
+    if lens.dtype != torch.int32 or lens.shape != (b,):
+        raise ValueError("lens must be int32 [b]")
+    c = _cache(K, V)
+    wsb = workspace.numel() * workspace.element_size()
+    if events is None:
+        _check("mqa_decode", _lib.mqa_decode(_ptr(q), q.shape[1], ctypes.byref(c), _ptr(lens),
+                                             float(scale), int(window), _ptr(out),
+                                             _ptr(workspace), wsb, _stream(q)))
+    else:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+        if not ev0.value or not ev1.value:
+            raise ValueError("timing events must be created (recorded once) before use")
+        _check("mqa_decode_timed", _lib.mqa_decode_timed(
+            _ptr(q), q.shape[1], ctypes.byref(c), _ptr(lens), float(scale), int(window),
+            _ptr(out), _ptr(workspace), wsb, _stream(q), ev0, ev1))
+    return out
+
+
+def prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None):
+    """Causal attention over a prompt; optionally fills the cache and lens."""
+    if out is None:
+        out = torch.empty_like(Q)
+    _dev(Q, K, V, out, cache_K, cache_V, lens)
+    b, n, h, dh = Q.shape
+    if K.dim() != 4 or K.shape[:2] != (b, n) or K.shape[3] != dh or V.shape != K.shape:
+        raise ValueError("K / V must be [b, n, G, d_h] matching Q")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype or out.dtype != Q.dtype or out.shape != Q.shape:
+        raise ValueError("Q, K, V and out must share one dtype and Q's shape")
+    if Q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {Q.dtype}")
+    G = K.shape[2]
+    cp = None
+    if cache_K is not None:
+        c = _cache(cache_K, cache_V)
+        cp = ctypes.byref(c)
+    if lens is not None and (lens.dtype != torch.int32 or lens.shape != (b,)):
+        raise ValueError("lens must be int32 [b]")
+    _check("mqa_prefill_causal", _lib.mqa_prefill_causal(
+        _ptr(Q), _ptr(K), _ptr(V), b, n, h, G, dh, _DTYPES[Q.dtype], float(scale), cp,
+        _ptr(lens), _ptr(out), _stream(Q)))
+    return out
+
+
+def check_lens(lens, m_cap):
+    """Synchronising host check that every lens[b] lies in [0, m_cap]."""
+    _dev(lens)
+    _check("mqa_check_lens", _lib.mqa_check_lens(_ptr(lens), lens.numel(), int(m_cap),
+                                                 _stream(lens)))
+
+
+class DecodeStep:
+    """One serving step -- optional kv_append, then decode -- over fixed tensors.
+
+    Validates the arguments once and keeps the ctypes argument lists, so each
+    call costs two C calls; used where per-step Python overhead would show
+    (benchmarks, HIP-graph capture).  The stream is read at call time, so a
+    step issued inside ``torch.cuda.graph`` is captured on the capture stream.
+    """
+
+    def __init__(self, q, K, V, lens, scale, out=None, workspace=None, k_new=None, v_new=None,
+                 window=0):
+        if workspace is None:
+            workspace = workspace_for(q.shape[1], K)
+        if out is None:
+            out = torch.empty_like(q)
+        self._keep = (q, K, V, lens, out, workspace, k_new, v_new)
+        b = K.shape[0]
+        if (k_new is None) != (v_new is None):
+            raise ValueError("give both k_new and v_new, or neither")
+        if k_new is not None:
+            _dev(k_new, v_new, K, V, lens)
+            if k_new.shape != (b, K.shape[2], K.shape[3]) or v_new.shape != k_new.shape:
+                raise ValueError("k_new / v_new must be [b, G, d_h]")
+            if k_new.dtype != K.dtype or v_new.dtype != K.dtype:
+                raise ValueError("k_new / v_new must have the cache dtype")
+        _dev(q, K, V, lens, out, workspace)
+        if q.dim() != 3 or q.shape[0] != b or q.shape[2] != K.shape[3] or q.dtype != K.dtype:
+            raise ValueError("q must be [b, h, d_h] in the cache dtype")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q")
+        if lens.dtype != torch.int32 or lens.shape != (b,):
+            raise ValueError("lens must be int32 [b]")
+        self.out = out
+        self.device = q.device
+        self._c = _cache(K, V)
+        cref = ctypes.byref(self._c)
+        wsb = workspace.numel() * workspace.element_size()
+        self._append = None
+        if k_new is not None:
+            self._append = (_ptr(k_new), _ptr(v_new), cref, _ptr(lens), None)
+        self._decode = (_ptr(q), q.shape[1], cref, _ptr(lens), float(scale), int(window),
+                        _ptr(out), _ptr(workspace), wsb)
+        lib_ = load()
+        self._fa, self._fd, self._ft = lib_.mqa_kv_append, lib_.mqa_decode, lib_.mqa_decode_timed
+
+    def __call__(self, events=None):
+        s = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        if self._append is not None:
+            rc = self._fa(*self._append, s)
+            if rc:
+                raise MQAError("mqa_kv_append", rc)
+        if events is None:
+            rc = self._fd(*self._decode, s)
+        else:
+            rc = self._ft(*self._decode, s, ctypes.c_void_p(events[0].cuda_event),
+                          ctypes.c_void_p(events[1].cuda_event))
+        if rc:
+            raise MQAError("mqa_decode", rc)
+        return self.out

@@ -1,0 +1,68 @@
+// mqa_internal.h -- host-side interface between the C-ABI layer (mqa_api.cpp)
+// and the kernel launchers (mqa_decode.hip, mqa_prefill.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mqa {
+
+// Largest split-K grid the decode may use; bounds the workspace.
+constexpr int kMaxDecodeGrid = 2048;
+// Cache positions per wave tile in the decode and prefill kernels.
+constexpr int kTileRows = 32;
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* lens;
+  void* o;
+  void* ws;
+  int b, h, G, dh, m_cap, window, dtype;
+  float scale;
+  hipEvent_t ev_begin = nullptr;  // optional, recorded around the split kernel
+  hipEvent_t ev_end = nullptr;
+};
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k;
+  void* v;
+  int32_t* lens;
+  int32_t* err_flag;
+  int b, m_cap;
+  int row_bytes;  // G * d_h * element size
+};
+
+struct PrefillParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  void* cache_k;  // nullable
+  void* cache_v;
+  int32_t* lens;  // nullable
+  int b, n, h, G, dh, dtype, m_cap;
+  float scale;
+};
+
+// Size in bytes of one split-K partial record for hg heads of width dh.
+size_t decode_record_bytes(int hg, int dh);
+// Byte offset of the first record in the workspace (after the schedule header).
+size_t decode_records_offset(int b);
+// Upper bound of the decode grid for these shapes (device independent).
+int decode_grid_cap(int b, int G, int m_cap);
+// Workspace bytes for mqa_decode.
+size_t decode_workspace_bytes(int b, int h, int G, int dh, int m_cap);
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int current_device_cus(int* device_out);
+
+}  // namespace mqa

@@ -1,0 +1,233 @@
+// mqa_prefill.hip -- gfx950 causal prefill for MQA/GQA:
+//   O[b,t,i,:] = softmax_{j<=t}(scale * Q[b,t,i,:] . K[b,j,g(i),:]) V[b,j,g(i),:]
+// (study notes section 1: O = softmax(QK^T/sqrt(d_h) + M) V, M = -inf above the
+// diagonal; paper review section 2.3 batched form with an additive mask).
+//
+// Columns.  A wave owns 32 query columns = rpw consecutive rows x hgp head
+// slots of one group (hgp = h/G rounded up to a power of two), so with MQA
+// (h/G = 32) one wave is one row with all its heads, and every column of a
+// row shares the causal limit.  Each column keeps its own online softmax; the
+// causal mask is a per-column limit on the key position.
+//
+// Workgroup.  NW waves cover NW*rpw consecutive rows of one (sequence, group)
+// and walk the key tiles [0, last row] once.  Per tile, the K rows and the V
+// rows (already transposed into the PV operand layout by an exact selection
+// MFMA) are staged in LDS once and read by all NW waves; LDS is double
+// buffered so the next tile's global loads overlap this tile's MFMAs.  Row
+// blocks are launched last-row-first so the longest causal rows start early.
+#include "mqa_device.h"
+#include "mqa_internal.h"
+
+namespace mqa {
+
+struct PrefillArgs {
+  const char* Q;
+  const char* K;
+  const char* V;
+  char* O;
+  int b, n, h, G, hg, hgp, rpw, nrb;
+  float scale_log2;
+};
+
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+  using S = TileShape<T, DH>;
+  constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
+  static_assert(NW > ND, "needs waves beyond the V transposers");
+  constexpr int NKW = NW - ND;                // waves staging K chunks
+  constexpr int KPW = (NQ + NKW - 1) / NKW;   // K chunks per K wave
+  constexpr int VPW = NQ / ND;                // V chunks per d block
+  __shared__ u32x4 s_k[2][NQ][64];
+  __shared__ u32x4 s_vt[2][ND][VTC][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  const int rb = a.nrb - 1 - (int)(blockIdx.x % a.nrb);
+  const int bg = blockIdx.x / a.nrb;
+  const int bi = bg / a.G, g = bg % a.G;
+  const int rows_per_block = NW * a.rpw;
+  const int r_begin = rb * rows_per_block;
+  if (r_begin >= a.n) return;
+  const int r_end = min(a.n, r_begin + rows_per_block);
+  const int ntiles = (r_end - 1) / kTileRows + 1;
+
+  const int w_row0 = r_begin + wave * a.rpw;
+  const int w_last = min(a.n - 1, w_row0 + a.rpw - 1);
+  const int w_tiles = (w_row0 < a.n) ? w_last / kTileRows + 1 : 0;
+  const int crow = w_row0 + col / a.hgp;
+  const int chead = col % a.hgp;
+  const bool col_ok = crow < a.n && chead < a.hg;
+
+  u32x4 qr[NQ];
+  if (col_ok) {
+    const char* qp = a.Q + (((size_t)bi * a.n + crow) * a.h + (size_t)g * a.hg + chead) * DH * sizeof(T);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) qr[c] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) qr[c] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  SelOps<T> sel;
+  sel.init(col, half);
+  const size_t rs = (size_t)a.G * DH * sizeof(T);
+  const size_t seq_off = ((size_t)bi * a.n * a.G + (size_t)g) * DH * sizeof(T);
+  const char* kseq = a.K + seq_off;
+  const char* vseq = a.V + seq_off;
+
+  const bool v_wave = wave < ND;
+  const int kw = wave - ND;
+  u32x4 ldv[VPW], ldk[KPW];
+
+  auto issue = [&](int tile) {
+    const int pos = tile * kTileRows + col;
+    const bool valid = pos < a.n;
+    if (v_wave) {
+      const char* p = vseq + (size_t)pos * rs;
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) {
+        const int c = wave * VPW + i;
+        ldv[i] = u32x4{0u, 0u, 0u, 0u};
+        if (valid) ldv[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
+      }
+    } else {
+      const char* p = kseq + (size_t)pos * rs;
+#pragma unroll
+      for (int i = 0; i < KPW; ++i) {
+        const int c = kw + i * NKW;
+        ldk[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < NQ && valid) ldk[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+    if (v_wave) {
+      u32x4 ops[VTC];
+      transpose_block<T, VPW>(ldv, 0, sel, ops);
+#pragma unroll
+      for (int k = 0; k < VTC; ++k) s_vt[buf][wave][k][lane] = ops[k];
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPW; ++i) {
+        const int c = kw + i * NKW;
+        if (c < NQ) s_k[buf][c][lane] = ldk[i];
+      }
+    }
+  };
+
+  WaveState<ND> st;
+  st.reset();
+  issue(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    commit(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1);
+    if (it < w_tiles) {
+      u32x4 kr[NQ];
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
+      const f32x16 s = tile_scores<T, NQ>(kr, qr);
+      const int pos0 = it * kTileRows;
+      float p[16];
+      if (pos0 + kTileRows - 1 <= w_row0)
+        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
+      else
+        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
+      PvOps<T> pv;
+      pv.set(p);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        u32x4 ops[VTC];
+#pragma unroll
+        for (int k = 0; k < VTC; ++k) ops[k] = s_vt[buf][d][k][lane];
+        st.o[d] = pv.apply(ops, st.o[d]);
+      }
+    }
+  }
+
+  const float l_tot = st.l + xor32(st.l);
+  if (col_ok) {
+    const float inv = 1.0f / l_tot;
+    T* op = reinterpret_cast<T*>(a.O) + (((size_t)bi * a.n + crow) * a.h + (size_t)g * a.hg + chead) * DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store4(op + 32 * d + 8 * r4 + 4 * half, st.o[d][4 * r4] * inv, st.o[d][4 * r4 + 1] * inv,
+               st.o[d][4 * r4 + 2] * inv, st.o[d][4 * r4 + 3] * inv);
+  }
+}
+
+// Copies the prompt's K/V rows into positions [0, n) of every sequence of the
+// cache and sets lens[b] = n.
+__global__ void prefill_cache_copy_kernel(const char* K, const char* V, char* ck, char* cv,
+                                          int32_t* lens, int b_copy, int b_lens, int n, int m_cap,
+                                          int row_bytes) {
+  const size_t per_seq = (size_t)n * row_bytes / 16;
+  const size_t total = (size_t)b_copy * per_seq;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const size_t bi = idx / per_seq, r = idx % per_seq;
+    const size_t src = bi * per_seq * 16 + r * 16;
+    const size_t dst = bi * (size_t)m_cap * row_bytes + r * 16;
+    *reinterpret_cast<u32x4*>(ck + dst) = *reinterpret_cast<const u32x4*>(K + src);
+    *reinterpret_cast<u32x4*>(cv + dst) = *reinterpret_cast<const u32x4*>(V + src);
+  }
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < (size_t)b_lens; i += stride)
+    lens[i] = n;
+}
+
+namespace {
+constexpr int kPrefillWaves = 8;
+
+template <typename T, int DH>
+hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+  const int row_bytes = p.G * p.dh * (int)sizeof(T);
+  if (p.cache_k || p.lens) {
+    const size_t chunks = (size_t)p.b * p.n * row_bytes / 16;
+    size_t blocks = (chunks + 255) / 256;
+    if (blocks < (size_t)(p.b + 255) / 256) blocks = (p.b + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(prefill_cache_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const char*)p.K, (const char*)p.V, (char*)p.cache_k, (char*)p.cache_v,
+                       p.lens, p.cache_k ? p.b : 0, p.lens ? p.b : 0, p.n, p.m_cap, row_bytes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  PrefillArgs a;
+  a.Q = (const char*)p.Q;
+  a.K = (const char*)p.K;
+  a.V = (const char*)p.V;
+  a.O = (char*)p.O;
+  a.b = p.b;
+  a.n = p.n;
+  a.h = p.h;
+  a.G = p.G;
+  a.hg = p.h / p.G;
+  int hgp = 1;
+  while (hgp < a.hg) hgp *= 2;
+  a.hgp = hgp;
+  a.rpw = 32 / hgp;
+  const int rows_per_block = kPrefillWaves * a.rpw;
+  a.nrb = (p.n + rows_per_block - 1) / rows_per_block;
+  a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  const size_t blocks = (size_t)p.b * p.G * a.nrb;
+  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves>), dim3((unsigned)blocks),
+                     dim3(kPrefillWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+  if (p.dtype == 1) {
+    if (p.dh == 128) return launch_prefill_t<__bf16, 128>(p, s);
+    return launch_prefill_t<__bf16, 64>(p, s);
+  }
+  if (p.dh == 128) return launch_prefill_t<float, 128>(p, s);
+  return launch_prefill_t<float, 64>(p, s);
+}
+
+}  // namespace mqa

@@ -33,3 +33,12 @@ def read_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return read_golden
+
+
+@pytest.fixture(scope="session")
+def libmqa_path():
+    """Path of the built libmqa.so, compiling it first when it is missing."""
+    from query_decode_attention_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    return B.LIB

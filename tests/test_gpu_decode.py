@@ -1,0 +1,299 @@
+"""GPU parity of the decode path (append + split-K decode + combine) against
+the fp64 oracle, on the same seeded inputs, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import announce, assert_parity
+from query_decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import query_decode_attention_amd as mqa
+
+
+def to_dev(d):
+    return {k: v.cuda() for k, v in d.items()}
+
+
+def run_decode(inp, scale, window=0, append=False):
+    """Runs (optional append +) decode on the GPU; returns (o, K, V, lens) on device."""
+    d = to_dev(inp)
+    if append:
+        mqa.kv_append(d["k_new"], d["v_new"], d["K"], d["V"], d["lens"])
+    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], scale, window=window)
+    torch.cuda.synchronize()
+    return o, d
+
+
+def oracle_step(inp, scale, window=0, append=False):
+    q, K, V, lens = inp["q"], inp["K"], inp["V"], inp["lens"].numpy().copy()
+    if append:
+        Kr, _ = oracle._raw(K)
+        Vr, _ = oracle._raw(V)
+        Kr, Vr = Kr.copy(), Vr.copy()
+        oracle.kv_append(inp["k_new"], inp["v_new"], Kr, Vr, lens)
+        K, V = Kr, Vr
+    return oracle.decode(q, K, V, lens, scale, window=window), lens
+
+
+def make(dtype, b, h, G, dh, m_cap, lo, hi, seed, append=False):
+    cfg = W.DecodeConfig("t", dtype, b, h, G, dh, m_cap, lo, hi, append, seed)
+    return cfg, W.decode_inputs(cfg)
+
+
+# ------------------------------------------------------------------ small grids
+
+
+CASES = [
+    # dtype, b, h, G, dh, m_cap, lens range
+    (torch.bfloat16, 3, 32, 1, 128, 300, 1, 300),       # MQA, ragged, tail tiles
+    (torch.bfloat16, 2, 32, 32, 128, 97, 60, 97),      # MHA (h/G = 1), m_cap not /32
+    (torch.bfloat16, 4, 16, 2, 128, 256, 1, 256),      # GQA h/G = 8
+    (torch.bfloat16, 2, 8, 1, 64, 160, 33, 160),       # d_h = 64
+    (torch.bfloat16, 5, 24, 1, 64, 64, 1, 64),         # h/G = 24 (not a power of two)
+    (torch.float32, 1, 4, 1, 64, 128, 128, 128),       # the tiny fp32 workload
+    (torch.float32, 3, 8, 2, 128, 200, 1, 200),        # fp32, d_h 128, GQA
+    (torch.float32, 2, 32, 1, 64, 130, 100, 130),      # fp32, full head block
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{str(c[0])[6:]}-b{c[1]}h{c[2]}G{c[3]}d{c[4]}m{c[5]}")
+def test_decode_parity_grid(case):
+    dtype, b, h, G, dh, m_cap, lo, hi = case
+    announce(f"decode grid {case}")
+    cfg, inp = make(dtype, b, h, G, dh, m_cap, lo, hi, seed=7000 + b * 31 + h + G + dh)
+    o, _ = run_decode(inp, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o, ref, dtype, f"grid {case}")
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_decode_many_sequences_multi_chunk_scan(append):
+    """b > 256 exercises the multi-chunk device scan of the schedule."""
+    announce(f"decode b=600 append={append}")
+    cfg, inp = make(torch.bfloat16, 600, 8, 1, 64, 96, 0, 95, seed=7100 + append)
+    o, _ = run_decode(inp, cfg.scale, append=append)
+    ref, _ = oracle_step(inp, cfg.scale, append=append)
+    assert_parity(o, ref, torch.bfloat16, "b=600")
+
+
+@pytest.mark.parametrize("window", [1, 7, 32, 33, 5000])
+def test_decode_local_window(window):
+    """Local attention over the last `window` positions (current + 31 previous is 32)."""
+    announce(f"decode window={window}")
+    cfg, inp = make(torch.bfloat16, 6, 32, 1, 128, 700, 1, 700, seed=7200 + window)
+    o, _ = run_decode(inp, cfg.scale, window=window, append=True)
+    ref, _ = oracle_step(inp, cfg.scale, window=window, append=True)
+    assert_parity(o, ref, torch.bfloat16, f"window {window}")
+
+
+# ------------------------------------------------------------------ workloads
+
+
+def test_c1_tiny_fp32():
+    announce("c1 full size")
+    inp = W.decode_inputs(W.C1)
+    o, _ = run_decode(inp, W.C1.scale)
+    ref, _ = oracle_step(inp, W.C1.scale)
+    assert_parity(o, ref, torch.float32, "c1")
+
+
+@pytest.mark.parametrize("cfg", [W.C2, W.C2_MHA], ids=lambda c: c.name)
+def test_c2_full(cfg):
+    announce(f"{cfg.name} full size")
+    inp = W.decode_inputs(cfg)
+    o, _ = run_decode(inp, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o, ref, torch.bfloat16, cfg.name)
+
+
+def test_c3_serving_full_with_append():
+    """b=64, h=32, ragged lens U{1..8192} + one append, exactly as timed."""
+    announce("c3 full size (append + decode)")
+    inp = W.decode_inputs(W.C3)
+    o, d = run_decode(inp, W.C3.scale, append=True)
+    ref, lens_ref = oracle_step(inp, W.C3.scale, append=True)
+    assert np.array_equal(d["lens"].cpu().numpy(), lens_ref)
+    assert_parity(o, ref, torch.bfloat16, "c3")
+
+
+def test_c4_gqa_full_sampled():
+    """b=32, h=64, G=8, m=32768: GPU runs the full step; the oracle checks a
+    seeded sample of 3 sequences (all 64 heads each)."""
+    announce("c4 full size, sampled sequences")
+    cfg = W.C4
+    inp = W.decode_inputs(cfg)
+    o, _ = run_decode(inp, cfg.scale)
+    o = o.cpu()
+    sample = [0, 17, 31]
+    sub = {k: inp[k][sample].contiguous() for k in ("q", "K", "V")}
+    ref = oracle.decode(sub["q"], sub["K"], sub["V"], inp["lens"][sample].numpy(), cfg.scale)
+    assert_parity(o[sample], ref, torch.bfloat16, "c4 sample")
+
+
+# ------------------------------------------------------------------ exact cases
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_single_position_returns_value_exactly(dtype):
+    announce(f"L=1 exact {dtype}")
+    cfg, inp = make(dtype, 4, 32, 4, 128, 50, 1, 1, seed=7300)
+    inp["q"] = (inp["q"].float() * 30).to(dtype)
+    o, _ = run_decode(inp, cfg.scale)
+    V = inp["V"]
+    exp = torch.stack([V[b, 0, torch.arange(32) // 8] for b in range(4)])
+    assert torch.equal(o.cpu(), exp)
+
+
+def test_append_then_decode_sees_only_the_new_token_when_empty():
+    announce("empty cache + append")
+    cfg, inp = make(torch.bfloat16, 3, 32, 1, 128, 40, 0, 0, seed=7310)
+    o, d = run_decode(inp, cfg.scale, append=True)
+    exp = inp["v_new"][:, 0:1, :].expand(3, 32, 128)
+    assert torch.equal(o.cpu(), exp)
+    assert d["lens"].cpu().tolist() == [1, 1, 1]
+
+
+def test_empty_rows_are_zero_and_lens_clamped():
+    announce("L=0 rows and lens > m_cap")
+    cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 70, 0, 0, seed=7320)
+    inp["lens"] = torch.tensor([0, 70, -3, 500], dtype=torch.int32)
+    o, _ = run_decode(inp, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert torch.equal(o[0].cpu(), torch.zeros(32, 128, dtype=torch.bfloat16))
+    assert torch.equal(o[2].cpu(), torch.zeros(32, 128, dtype=torch.bfloat16))
+    assert_parity(o, ref, torch.bfloat16, "clamp")
+
+
+def test_zero_scale_gives_mean_and_constant_v():
+    announce("scale=0 mean; constant V")
+    cfg, inp = make(torch.bfloat16, 3, 32, 1, 128, 500, 100, 500, seed=7330)
+    o, _ = run_decode(inp, 0.0)
+    ref, _ = oracle_step(inp, 0.0)
+    assert_parity(o, ref, torch.bfloat16, "scale 0")
+    inp["V"] = torch.full_like(inp["V"], 0.375)
+    o, _ = run_decode(inp, cfg.scale)
+    assert (o.float().cpu() - 0.375).abs().max().item() <= 2e-3
+
+
+def test_large_logits_stay_finite():
+    """q x 20: logits with std ~ 20 overflow fp32 exp without the running max."""
+    announce("q x 20 stress")
+    cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 2000, 1000, 2000, seed=7340)
+    inp["q"] = (inp["q"].float() * 20).to(torch.bfloat16)
+    o, _ = run_decode(inp, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o, ref, torch.bfloat16, "q x 20")
+
+
+def test_negative_scale():
+    announce("negative scale")
+    cfg, inp = make(torch.bfloat16, 2, 32, 2, 64, 300, 200, 300, seed=7350)
+    o, _ = run_decode(inp, -0.3)
+    ref, _ = oracle_step(inp, -0.3)
+    assert_parity(o, ref, torch.bfloat16, "scale -0.3")
+
+
+# ------------------------------------------------------------------ invariants
+
+
+def test_poison_beyond_lens_and_determinism():
+    announce("poison + determinism")
+    cfg, inp = make(torch.bfloat16, 8, 32, 1, 128, 1000, 1, 999, seed=7400)
+    o1, _ = run_decode(inp, cfg.scale)
+    o2, _ = run_decode(inp, cfg.scale)
+    assert torch.equal(o1, o2)
+    poisoned = dict(inp)
+    poisoned["K"] = W.poison_beyond(inp["K"], inp["lens"])
+    poisoned["V"] = W.poison_beyond(inp["V"], inp["lens"])
+    o3, _ = run_decode(poisoned, cfg.scale)
+    assert torch.isfinite(o3.float()).all()
+    assert torch.equal(o1, o3)
+
+
+def test_mqa_equals_tied_mha_on_gpu():
+    announce("MQA == tied MHA")
+    cfg, inp = make(torch.bfloat16, 3, 8, 1, 128, 400, 100, 400, seed=7410)
+    o1, _ = run_decode(inp, cfg.scale)
+    tied = dict(inp)
+    tied["K"] = inp["K"].expand(3, 400, 8, 128).contiguous()
+    tied["V"] = inp["V"].expand(3, 400, 8, 128).contiguous()
+    o2, _ = run_decode(tied, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o1, ref, torch.bfloat16, "mqa")
+    assert_parity(o2, ref, torch.bfloat16, "tied mha")
+
+
+def test_append_is_bit_exact_and_flags_full_caches():
+    announce("append bit-exact")
+    cfg, inp = make(torch.bfloat16, 5, 32, 2, 128, 64, 0, 64, seed=7420)
+    inp["lens"] = torch.tensor([0, 63, 64, 10, 70], dtype=torch.int32)
+    d = to_dev(inp)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mqa.kv_append(d["k_new"], d["v_new"], d["K"], d["V"], d["lens"], err_flag=err)
+    torch.cuda.synchronize()
+    Kr, _ = oracle._raw(inp["K"])
+    Vr, _ = oracle._raw(inp["V"])
+    Kr, Vr = Kr.copy(), Vr.copy()
+    lens = inp["lens"].numpy().copy()
+    over = oracle.kv_append(inp["k_new"], inp["v_new"], Kr, Vr, lens)
+    assert over == 2 and err.item() == 1
+    assert np.array_equal(d["lens"].cpu().numpy(), lens)
+    gk = d["K"].cpu().view(torch.int16).numpy().view(np.uint16)
+    gv = d["V"].cpu().view(torch.int16).numpy().view(np.uint16)
+    assert gk.tobytes() == Kr.tobytes() and gv.tobytes() == Vr.tobytes()
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.check_lens(d["lens"], 64)                # lens[4] = 70 stays beyond m_cap
+    assert e.value.status == -8
+    mqa.check_lens(d["lens"][:4].contiguous(), 64)
+
+
+def test_serial_decode_loop_matches_oracle():
+    """Ten append+decode steps with a growing cache (the serial token loop)."""
+    announce("10-step loop")
+    cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 300, 20, 250, seed=7430)
+    d = to_dev(inp)
+    Kr, _ = oracle._raw(inp["K"])
+    Vr, _ = oracle._raw(inp["V"])
+    Kr, Vr = Kr.copy(), Vr.copy()
+    lens = inp["lens"].numpy().copy()
+    g = torch.Generator().manual_seed(99)
+    ws = mqa.workspace_for(32, d["K"])
+    for step in range(10):
+        kn = torch.randn(4, 1, 128, generator=g).to(torch.bfloat16)
+        vn = torch.randn(4, 1, 128, generator=g).to(torch.bfloat16)
+        q = torch.randn(4, 32, 128, generator=g).to(torch.bfloat16)
+        mqa.kv_append(kn.cuda(), vn.cuda(), d["K"], d["V"], d["lens"])
+        o = mqa.decode(q.cuda(), d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
+        oracle.kv_append(kn, vn, Kr, Vr, lens)
+        ref = oracle.decode(q, Kr, Vr, lens, cfg.scale)
+        assert_parity(o, ref, torch.bfloat16, f"loop step {step}")
+
+
+# ------------------------------------------------------------------ errors
+
+
+def test_argument_errors_raise():
+    announce("argument errors")
+    K = torch.zeros(2, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
+    lens = torch.ones(2, dtype=torch.int32, device="cuda")
+    q = torch.zeros(2, 6, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.decode(torch.zeros(2, 5, 128, dtype=torch.bfloat16, device="cuda"), K, K, lens, 1.0)
+    assert e.value.status == -2                      # G does not divide h
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.decode(q, K, K, lens, 1.0, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == -5                      # workspace too small
+    Kb = torch.zeros(2, 64, 1, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.decode(torch.zeros(2, 64, 128, dtype=torch.bfloat16, device="cuda"), Kb, Kb, lens, 1.0)
+    assert e.value.status == -2                      # h/G = 64 > 32
+    K96 = torch.zeros(2, 64, 1, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.decode(torch.zeros(2, 4, 96, dtype=torch.bfloat16, device="cuda"), K96, K96, lens, 1.0)
+    assert e.value.status == -3                      # d_h = 96

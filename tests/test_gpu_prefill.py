@@ -1,0 +1,89 @@
+"""GPU parity of the causal prefill against the fp64 oracle (full masked-row
+route), plus its cache hand-off to decode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import announce, assert_parity
+from query_decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import query_decode_attention_amd as mqa
+
+
+def make(dtype, b, n, h, G, dh, seed):
+    cfg = W.PrefillConfig("t", dtype, b, n, h, G, dh, seed)
+    return cfg, W.prefill_inputs(cfg)
+
+
+CASES = [
+    (torch.bfloat16, 2, 100, 32, 1, 128),   # MQA, ragged last tile
+    (torch.bfloat16, 1, 257, 32, 4, 128),   # GQA h/G = 8 (4 rows per wave)
+    (torch.bfloat16, 2, 70, 4, 4, 64),      # MHA h/G = 1 (32 rows per wave)
+    (torch.bfloat16, 1, 64, 12, 1, 64),     # h/G = 12 padded to 16
+    (torch.float32, 1, 90, 8, 2, 128),
+    (torch.float32, 2, 33, 32, 1, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{str(c[0])[6:]}-b{c[1]}n{c[2]}h{c[3]}G{c[4]}d{c[5]}")
+def test_prefill_parity_grid(case):
+    dtype, b, n, h, G, dh = case
+    announce(f"prefill grid {case}")
+    cfg, inp = make(dtype, b, n, h, G, dh, seed=8000 + n + h + G)
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], cfg.scale)
+    assert_parity(O, ref, dtype, f"prefill {case}")
+
+
+def test_prefill_first_row_is_first_value():
+    announce("prefill row 0 exact")
+    cfg, inp = make(torch.bfloat16, 2, 40, 32, 1, 128, seed=8100)
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale).cpu()
+    for b in range(2):
+        assert torch.equal(O[b, 0], inp["V"][b, 0, 0].expand(32, 128))
+
+
+def test_c5_full_size_sampled_rows():
+    """b=4, n=4096, h=32, G=1: the GPU computes everything; the oracle checks
+    288 seeded rows including the first and last of every sequence."""
+    announce("c5 full size, sampled rows")
+    cfg = W.C5
+    inp = W.prefill_inputs(cfg)
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale).cpu()
+    g = torch.Generator().manual_seed(5)
+    rows = set()
+    for b in range(cfg.b):
+        rows.update({b * cfg.n, b * cfg.n + cfg.n - 1, b * cfg.n + 31, b * cfg.n + 32})
+    rows.update(torch.randint(0, cfg.b * cfg.n, (272,), generator=g).tolist())
+    rows = sorted(rows)
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], cfg.scale, rows=rows)
+    got = O.reshape(cfg.b * cfg.n, cfg.h, cfg.dh)[rows]
+    assert_parity(got, ref, torch.bfloat16, f"c5 {len(rows)} rows")
+
+
+def test_prefill_fills_cache_and_hands_off_to_decode():
+    """Prefill writes K/V into the cache and sets lens = n; a decode step with
+    query Q[:, t] over a cache of t+1 rows equals prefill row t."""
+    announce("prefill -> cache -> decode")
+    cfg, inp = make(torch.bfloat16, 2, 150, 32, 1, 128, seed=8200)
+    m_cap = 200
+    Kc = torch.full((2, m_cap, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.full_like(Kc, float("nan"))
+    lens = torch.zeros(2, dtype=torch.int32, device="cuda")
+    Q, K, V = inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda()
+    O = mqa.prefill_causal(Q, K, V, cfg.scale, cache_K=Kc, cache_V=Vc, lens=lens)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [150, 150]
+    assert torch.equal(Kc[:, :150].cpu(), inp["K"]) and torch.equal(Vc[:, :150].cpu(), inp["V"])
+    assert torch.isnan(Kc[:, 150:].float()).all()
+    for t in (0, 31, 32, 149):
+        lt = torch.full((2,), t + 1, dtype=torch.int32, device="cuda")
+        o = mqa.decode(Q[:, t].contiguous(), Kc, Vc, lt, cfg.scale)
+        ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], cfg.scale, rows=[t, 150 + t])
+        assert_parity(o, ref, torch.bfloat16, f"decode row {t}")
+        assert_parity(O[:, t], ref, torch.bfloat16, f"prefill row {t}")
