@@ -50,7 +50,7 @@ def log(msg):
 class DecodeBench:
     """R rotated copies of one decode workload living in HBM."""
 
-    def __init__(self, cfg, R, torch, mqa, seed_base=0):
+    def __init__(self, cfg, R, torch, mqa, seed_base=0, fused=True):
         self.cfg, self.R, self.torch = cfg, R, torch
         dev = torch.device("cuda")
         b, h, G, dh, m_cap = cfg.b, cfg.h, cfg.G, cfg.dh, cfg.m_cap
@@ -75,7 +75,7 @@ class DecodeBench:
         for c in self.copies:
             kw = dict(k_new=c["kn"], v_new=c["vn"]) if cfg.append else {}
             self.steps.append(mqa.DecodeStep(c["q"], c["K"], c["V"], c["lens"], cfg.scale,
-                                             out=self.out, workspace=self.ws, **kw))
+                                             out=self.out, workspace=self.ws, fused=fused, **kw))
         self.appends = [0] * R   # appends issued per copy so far
         self.elem = 2 if cfg.dtype == torch.bfloat16 else 4
 
@@ -148,9 +148,9 @@ class DecodeBench:
         return dt, kv, tot, fl, n_steps
 
     def kernel_timing(self, n):
-        """Average split-K kernel duration (HIP events on the launch stream) and its
-        algorithmic bytes per launch, over n eager steps queued behind a GPU sleep
-        so that launches never wait for the host."""
+        """Average duration of the decode kernel (HIP events recorded on its launch
+        stream right around it) and its algorithmic bytes per launch, over n eager
+        steps queued behind a GPU sleep so that launches never wait for the host."""
         torch = self.torch
         evs = []
         for _ in range(n):
@@ -161,7 +161,7 @@ class DecodeBench:
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * 0.02))      # ~20 ms of GPU spin: launches queue up
         kv = 0
-        other = 2 * self.cfg.b * self.cfg.h * self.cfg.dh * self.elem + 4 * self.cfg.b
+        other = self.other_bytes()
         for i in range(n):
             r = i % self.R
             self.appends[r] += 1 if self.cfg.append else 0
@@ -264,6 +264,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--kernel-steps", type=int, default=64)
+    ap.add_argument("--two-call", action="store_true",
+                    help="append with mqa_kv_append, then mqa_decode (two launches per step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,16 +283,16 @@ def main():
     use_graph = not args.eager
 
     log("headline: serving decode c3 (b=64, h=32, G=1, d_h=128, lens U[1,8192] + append)")
-    head = DecodeBench(W.C3, args.rotate, torch, mqa)
+    head = DecodeBench(W.C3, args.rotate, torch, mqa, fused=not args.two_call)
     res = decode_result(head, args.steps, args.warmup, use_graph)
     log(f"headline {res['steps_per_s']:.1f} steps/s, {res['kv_gbps']:.1f} GB/s KV "
         f"({100 * res['kv_frac_of_peak']:.1f}% of 8 TB/s)")
     kdur, kbytes, kkv = head.kernel_timing(args.kernel_steps)
     achieved = kbytes / kdur / 1e9
-    log(f"split kernel avg {kdur * 1e6:.2f} us, {achieved:.1f} GB/s")
+    log(f"decode kernel avg {kdur * 1e6:.2f} us, {achieved:.1f} GB/s")
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                    kernel="decode_split_kernel<bf16,128,8>",
+                    kernel="decode_kernel<bf16,128,8>",
                     avg_launch_us=round(kdur * 1e6, 3),
                     algorithmic_bytes_per_launch=int(kbytes))
     del head
@@ -335,10 +337,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "serving MQA decode: append + split-K decode + combine",
+        "config": {"workload": "serving MQA decode: kv append + decode (split-K, in-kernel combine)",
                    "b": 64, "h": 32, "G": 1, "d_h": 128, "lens": "uniform [1,8192] + 1 append",
                    "m_cap": W.C3.m_cap, "rotated_caches": args.rotate,
-                   "launch": "eager" if args.eager else "hip-graph"},
+                   "launch": ("eager" if args.eager else "hip-graph") +
+                             (", two calls" if args.two_call else ", one fused kernel")},
         "kv_gbps": round(res["kv_gbps"], 1),
         "kv_frac_of_hbm_peak": round(res["kv_frac_of_peak"], 4),
         "roofline": roofline,

@@ -79,17 +79,18 @@ typedef struct {
 int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache,
                   int32_t* lens, int32_t* err_flag, void* stream);
 
-/* Bytes of device workspace mqa_decode needs for `h` query heads over
- * `cache` (split-K partial results plus a small schedule header).  Depends
- * only on the shapes, never on the device or on lens.  Returns 0 when the
- * arguments are invalid. */
+/* Bytes of device workspace a decode needs for `h` query heads over `cache`:
+ * a small schedule header (b + 1 ints) followed by the split-K partial
+ * results.  Depends only on the shapes, never on the device or on lens.
+ * Returns 0 when the arguments are invalid. */
 size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache);
 
 /* mqa_decode -- one decode step (study notes section 4:
  * o_i = softmax(q_i K^T * scale) V; paper review section 3 einsums
- * "bhk,bmk->bhm", softmax, "bhm,bmv->bhv").
+ * "bhk,bmk->bhm", softmax, "bhm,bmv->bhv").  Two kernel launches: the
+ * split-K attention, then the exact merge of segments it split.
  *   q      : device [b][h][d_h].
- *   lens   : device int32 [b]; sequence b attends over positions
+ *   lens   : device int32 [b] (read only); sequence b attends over positions
  *            [max(0, L - window), L) with L = clamp(lens[b], 0, m_cap).
  *            Positions at or beyond L are never read.  L == 0 gives o = 0.
  *   scale  : logit multiplier (1/sqrt(d_h) in the study notes; the paper
@@ -99,22 +100,35 @@ size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache);
  *            is w = 32).
  *   o      : device [b][h][d_h], written.
  *   workspace, ws_bytes : device scratch of >= mqa_decode_workspace_size()
- *            bytes, 16-byte aligned; contents need no initialisation and are
- *            clobbered.  Two calls that share a workspace must be ordered.
- * Launches two kernels (split-K attention, then the exact combine). */
+ *            bytes, 16-byte aligned; needs no initialisation; clobbered.
+ *            Calls that share a workspace must be ordered (same stream, or
+ *            synchronised). */
 int mqa_decode(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens,
                float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
                void* stream);
 
-/* mqa_decode_timed -- mqa_decode plus kernel-level timing: the optional
- * hipEvent_t handles ev_begin / ev_end (NULL = skip) are recorded on `stream`
- * immediately before and after the split-K attention kernel, the step's
- * dominant kernel, so a caller can time it with hipEventElapsedTime.  The
- * events must have been created for `stream`'s device.  Results are identical
- * to mqa_decode. */
-int mqa_decode_timed(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens,
-                     float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
-                     void* stream, void* ev_begin, void* ev_end);
+/* mqa_append_decode -- mqa_kv_append followed by mqa_decode with identical
+ * results, but without the separate append launch (the attention kernel
+ * reads the new row and stores it into the cache): sequence b attends over its cache
+ * plus the new row (k_new[b], v_new[b]) at position lens[b]; the new row is
+ * stored into the cache and lens[b] is incremented.  A sequence whose cache
+ * is full (lens[b] >= m_cap) or whose lens[b] < 0 gets no new row, keeps its
+ * lens, attends over clamp(lens[b], 0, m_cap) positions, and sets *err_flag
+ * (optional) to 1. */
+int mqa_append_decode(const void* q, const void* k_new, const void* v_new, int32_t h,
+                      const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                      int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/* mqa_decode_ex -- the general form of the two calls above.  k_new / v_new
+ * NULL selects mqa_decode, non-NULL selects mqa_append_decode.  ev_begin /
+ * ev_end are optional hipEvent_t handles (NULL = skip) recorded on `stream`
+ * immediately before and after the decode kernel, so a caller can time that
+ * kernel (the dominant one of the step) alone; they must belong to the
+ * stream's device. */
+int mqa_decode_ex(const void* q, const void* k_new, const void* v_new, int32_t h,
+                  const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                  int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream,
+                  void* ev_begin, void* ev_end);
 
 /* mqa_prefill_causal -- causal attention over a whole prompt (study notes
  * section 1: O = softmax(Q K^T / sqrt(d_h) + M) V with M_ij = -inf for j > i;

@@ -9,8 +9,9 @@ the library is missing.  PyTorch supplies device memory and streams only.
 
 Entry points (same names as the C ABI, minus the ``mqa_`` prefix):
   kv_append(k_new, v_new, K, V, lens, err_flag=None)
-  decode_workspace_size(h, K)
+  decode_workspace_size(h, K) / workspace_for(h, K)
   decode(q, K, V, lens, scale, window=0, out=None, workspace=None)
+  append_decode(q, k_new, v_new, K, V, lens, scale, ...)   (append fused in)
   prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None)
   check_lens(lens, m_cap)
   strerror(status)
@@ -29,6 +30,11 @@ LIB_PATH = os.path.join(_HERE, "libmqa.so")
 
 MQA_F32, MQA_BF16 = 0, 1
 _DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
+
+# Symbols include/mqa.h declares (tests check the library exports each one).
+EXPORTED = ("mqa_kv_append", "mqa_decode_workspace_size",
+            "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal",
+            "mqa_check_lens", "mqa_strerror", "mqa_abi_version")
 
 
 class MQAError(RuntimeError):
@@ -53,22 +59,22 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     CP = ctypes.POINTER(_Cache)
-    lib.mqa_kv_append.argtypes = [P, P, CP, P, P, P]
-    lib.mqa_kv_append.restype = ctypes.c_int
-    lib.mqa_decode_workspace_size.argtypes = [I32, CP]
-    lib.mqa_decode_workspace_size.restype = SZ
-    lib.mqa_decode.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P]
-    lib.mqa_decode.restype = ctypes.c_int
-    lib.mqa_decode_timed.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P, P, P]
-    lib.mqa_decode_timed.restype = ctypes.c_int
-    lib.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
-    lib.mqa_prefill_causal.restype = ctypes.c_int
-    lib.mqa_check_lens.argtypes = [P, I32, I32, P]
-    lib.mqa_check_lens.restype = ctypes.c_int
-    lib.mqa_strerror.argtypes = [ctypes.c_int]
-    lib.mqa_strerror.restype = ctypes.c_char_p
-    lib.mqa_abi_version.argtypes = []
-    lib.mqa_abi_version.restype = ctypes.c_int
+    sig = {
+        "mqa_kv_append": ([P, P, CP, P, P, P], ctypes.c_int),
+        "mqa_decode_workspace_size": ([I32, CP], SZ),
+        "mqa_decode": ([P, I32, CP, P, F, I32, P, P, SZ, P], ctypes.c_int),
+        "mqa_append_decode": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P], ctypes.c_int),
+        "mqa_decode_ex": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P], ctypes.c_int),
+        "mqa_prefill_causal": ([P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P],
+                               ctypes.c_int),
+        "mqa_check_lens": ([P, I32, I32, P], ctypes.c_int),
+        "mqa_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "mqa_abi_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
     return lib
 
 
@@ -89,10 +95,6 @@ class _LazyLib:
 
 
 _lib = _LazyLib()
-
-# Symbols include/mqa.h declares (tests check the library exports each one).
-EXPORTED = ("mqa_kv_append", "mqa_decode_workspace_size", "mqa_decode", "mqa_decode_timed",
-            "mqa_prefill_causal", "mqa_check_lens", "mqa_strerror", "mqa_abi_version")
 
 
 def lib():
@@ -116,8 +118,8 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _dev(*ts):
@@ -145,9 +147,12 @@ def _cache(K, V):
     return _Cache(K.data_ptr(), V.data_ptr(), b, m_cap, G, dh, _DTYPES[K.dtype])
 
 
-def kv_append(k_new, v_new, K, V, lens, err_flag=None):
-    """K[b, lens[b]] = k_new[b]; V likewise; lens[b] += 1 (in place, async)."""
-    dev = _dev(k_new, v_new, K, V, lens, err_flag)
+def _shape_only(K):
+    b, m_cap, G, dh = K.shape
+    return _Cache(None, None, b, m_cap, G, dh, _DTYPES.get(K.dtype, -1))
+
+
+def _check_new_rows(k_new, v_new, K, lens):
     b, _, G, dh = K.shape
     if k_new.shape != (b, G, dh) or v_new.shape != (b, G, dh):
         raise ValueError("k_new / v_new must be [b, G, d_h]")
@@ -155,16 +160,17 @@ def kv_append(k_new, v_new, K, V, lens, err_flag=None):
         raise ValueError("k_new / v_new must have the cache dtype")
     if lens.dtype != torch.int32 or lens.shape != (b,):
         raise ValueError("lens must be int32 [b]")
+
+
+def kv_append(k_new, v_new, K, V, lens, err_flag=None):
+    """K[b, lens[b]] = k_new[b]; V likewise; lens[b] += 1 (in place, async)."""
+    dev = _dev(k_new, v_new, K, V, lens, err_flag)
+    _check_new_rows(k_new, v_new, K, lens)
     if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1):
         raise ValueError("err_flag must be an int32 tensor")
     c = _cache(K, V)
     _check("mqa_kv_append", _lib.mqa_kv_append(_ptr(k_new), _ptr(v_new), ctypes.byref(c),
-                                                 _ptr(lens), _ptr(err_flag), _stream(K)))
-
-
-def _shape_only(K):
-    b, m_cap, G, dh = K.shape
-    return _Cache(None, None, b, m_cap, G, dh, _DTYPES.get(K.dtype, -1))
+                                                 _ptr(lens), _ptr(err_flag), _stream(dev)))
 
 
 def decode_workspace_size(h: int, K) -> int:
@@ -175,23 +181,20 @@ def decode_workspace_size(h: int, K) -> int:
 
 
 def workspace_for(h: int, K):
-    """Allocate a decode workspace (uint8 device tensor) for these shapes."""
-    return torch.empty(decode_workspace_size(h, K), dtype=torch.uint8, device=K.device)
+    """Allocate a decode workspace (uint8 device tensor; needs no initialisation).
+
+    Invalid shapes give a 1-byte tensor, so that the decode call itself
+    reports the exact status."""
+    n = _lib.mqa_decode_workspace_size(int(h), ctypes.byref(_shape_only(K)))
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=K.device)
 
 
-def decode(q, K, V, lens, scale, window=0, out=None, workspace=None, events=None):
-    """One decode step: o[b,i] = softmax(scale * q[b,i] . K[b,:L,g(i)]) V[b,:L,g(i)].
-
-    events: optional (begin, end) torch.cuda.Event pair, already created on
-    q's device, recorded around the split-K attention kernel.
-    """
+def _decode_call(q, k_new, v_new, K, V, lens, scale, window, out, workspace, err_flag, events):
     if workspace is None:
-        n = _lib.mqa_decode_workspace_size(int(q.shape[1]), ctypes.byref(_shape_only(K)))
-        # invalid shapes give n == 0: the C call below then reports the exact status
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=K.device)
+        workspace = workspace_for(q.shape[1], K)
     if out is None:
         out = torch.empty_like(q)
-    _dev(q, K, V, lens, out, workspace)
+    dev = _dev(q, k_new, v_new, K, V, lens, out, workspace, err_flag)
     b, m_cap, G, dh = K.shape
     if q.dim() != 3 or q.shape[0] != b or q.shape[2] != dh:
         raise ValueError("q must be [b, h, d_h] matching the cache")
@@ -199,27 +202,44 @@ def decode(q, K, V, lens, scale, window=0, out=None, workspace=None, events=None
         raise ValueError("q / out must match the cache dtype and q's shape")
     if lens.dtype != torch.int32 or lens.shape != (b,):
         raise ValueError("lens must be int32 [b]")
+    if k_new is not None:
+        _check_new_rows(k_new, v_new, K, lens)
     c = _cache(K, V)
-    wsb = workspace.numel() * workspace.element_size()
-    if events is None:
-        _check("mqa_decode", _lib.mqa_decode(_ptr(q), q.shape[1], ctypes.byref(c), _ptr(lens),
-                                             float(scale), int(window), _ptr(out),
-                                             _ptr(workspace), wsb, _stream(q)))
-    else:
+    ev0 = ev1 = None
+    if events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in events)
         if not ev0.value or not ev1.value:
             raise ValueError("timing events must be created (recorded once) before use")
-        _check("mqa_decode_timed", _lib.mqa_decode_timed(
-            _ptr(q), q.shape[1], ctypes.byref(c), _ptr(lens), float(scale), int(window),
-            _ptr(out), _ptr(workspace), wsb, _stream(q), ev0, ev1))
+    _check("mqa_decode_ex", _lib.mqa_decode_ex(
+        _ptr(q), _ptr(k_new), _ptr(v_new), q.shape[1], ctypes.byref(c), _ptr(lens),
+        _ptr(err_flag), float(scale), int(window), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev), ev0, ev1))
     return out
+
+
+def decode(q, K, V, lens, scale, window=0, out=None, workspace=None, events=None):
+    """One decode step: o[b,i] = softmax(scale * q[b,i] . K[b,:L,g(i)]) V[b,:L,g(i)].
+
+    events: optional (begin, end) torch.cuda.Event pair, already created on
+    q's device, recorded around the decode kernel.
+    """
+    return _decode_call(q, None, None, K, V, lens, scale, window, out, workspace, None, events)
+
+
+def append_decode(q, k_new, v_new, K, V, lens, scale, window=0, out=None, workspace=None,
+                  err_flag=None, events=None):
+    """kv_append followed by decode, with the append done by the decode kernels."""
+    if k_new is None or v_new is None:
+        raise ValueError("append_decode needs k_new and v_new")
+    return _decode_call(q, k_new, v_new, K, V, lens, scale, window, out, workspace, err_flag,
+                        events)
 
 
 def prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None):
     """Causal attention over a prompt; optionally fills the cache and lens."""
     if out is None:
         out = torch.empty_like(Q)
-    _dev(Q, K, V, out, cache_K, cache_V, lens)
+    dev = _dev(Q, K, V, out, cache_K, cache_V, lens)
     b, n, h, dh = Q.shape
     if K.dim() != 4 or K.shape[:2] != (b, n) or K.shape[3] != dh or V.shape != K.shape:
         raise ValueError("K / V must be [b, n, G, d_h] matching Q")
@@ -236,43 +256,42 @@ def prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=No
         raise ValueError("lens must be int32 [b]")
     _check("mqa_prefill_causal", _lib.mqa_prefill_causal(
         _ptr(Q), _ptr(K), _ptr(V), b, n, h, G, dh, _DTYPES[Q.dtype], float(scale), cp,
-        _ptr(lens), _ptr(out), _stream(Q)))
+        _ptr(lens), _ptr(out), _stream(dev)))
     return out
 
 
 def check_lens(lens, m_cap):
     """Synchronising host check that every lens[b] lies in [0, m_cap]."""
-    _dev(lens)
+    dev = _dev(lens)
     _check("mqa_check_lens", _lib.mqa_check_lens(_ptr(lens), lens.numel(), int(m_cap),
-                                                 _stream(lens)))
+                                                 _stream(dev)))
 
 
 class DecodeStep:
-    """One serving step -- optional kv_append, then decode -- over fixed tensors.
+    """One serving step over fixed tensors: append + decode (append fused into
+    the decode by default, or kv_append then decode with ``fused=False``), or
+    a plain decode when k_new/v_new are None.
 
-    Validates the arguments once and keeps the ctypes argument lists, so each
-    call costs two C calls; used where per-step Python overhead would show
-    (benchmarks, HIP-graph capture).  The stream is read at call time, so a
-    step issued inside ``torch.cuda.graph`` is captured on the capture stream.
+    Validates the arguments once and keeps the ctypes argument lists, so a
+    call costs one or two C calls; used where per-step Python overhead would
+    show (benchmarks, HIP-graph capture).  The stream is read at call time,
+    so a step issued inside ``torch.cuda.graph`` is captured on the capture
+    stream.
     """
 
     def __init__(self, q, K, V, lens, scale, out=None, workspace=None, k_new=None, v_new=None,
-                 window=0):
+                 window=0, fused=True):
         if workspace is None:
             workspace = workspace_for(q.shape[1], K)
         if out is None:
             out = torch.empty_like(q)
         self._keep = (q, K, V, lens, out, workspace, k_new, v_new)
-        b = K.shape[0]
         if (k_new is None) != (v_new is None):
             raise ValueError("give both k_new and v_new, or neither")
+        self.device = _dev(q, K, V, lens, out, workspace, k_new, v_new)
+        b = K.shape[0]
         if k_new is not None:
-            _dev(k_new, v_new, K, V, lens)
-            if k_new.shape != (b, K.shape[2], K.shape[3]) or v_new.shape != k_new.shape:
-                raise ValueError("k_new / v_new must be [b, G, d_h]")
-            if k_new.dtype != K.dtype or v_new.dtype != K.dtype:
-                raise ValueError("k_new / v_new must have the cache dtype")
-        _dev(q, K, V, lens, out, workspace)
+            _check_new_rows(k_new, v_new, K, lens)
         if q.dim() != 3 or q.shape[0] != b or q.shape[2] != K.shape[3] or q.dtype != K.dtype:
             raise ValueError("q must be [b, h, d_h] in the cache dtype")
         if out.shape != q.shape or out.dtype != q.dtype:
@@ -280,17 +299,17 @@ class DecodeStep:
         if lens.dtype != torch.int32 or lens.shape != (b,):
             raise ValueError("lens must be int32 [b]")
         self.out = out
-        self.device = q.device
         self._c = _cache(K, V)
         cref = ctypes.byref(self._c)
         wsb = workspace.numel() * workspace.element_size()
-        self._append = None
-        if k_new is not None:
-            self._append = (_ptr(k_new), _ptr(v_new), cref, _ptr(lens), None)
-        self._decode = (_ptr(q), q.shape[1], cref, _ptr(lens), float(scale), int(window),
-                        _ptr(out), _ptr(workspace), wsb)
         lib_ = load()
-        self._fa, self._fd, self._ft = lib_.mqa_kv_append, lib_.mqa_decode, lib_.mqa_decode_timed
+        self._fa, self._fx = lib_.mqa_kv_append, lib_.mqa_decode_ex
+        self._append = None
+        new = (_ptr(k_new), _ptr(v_new)) if (k_new is not None and fused) else (None, None)
+        if k_new is not None and not fused:
+            self._append = (_ptr(k_new), _ptr(v_new), cref, _ptr(lens), None)
+        self._decode = (_ptr(q),) + new + (q.shape[1], cref, _ptr(lens), None, float(scale),
+                                           int(window), _ptr(out), _ptr(workspace), wsb)
 
     def __call__(self, events=None):
         s = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
@@ -299,10 +318,10 @@ class DecodeStep:
             if rc:
                 raise MQAError("mqa_kv_append", rc)
         if events is None:
-            rc = self._fd(*self._decode, s)
+            rc = self._fx(*self._decode, s, None, None)
         else:
-            rc = self._ft(*self._decode, s, ctypes.c_void_p(events[0].cuda_event),
+            rc = self._fx(*self._decode, s, ctypes.c_void_p(events[0].cuda_event),
                           ctypes.c_void_p(events[1].cuda_event))
         if rc:
-            raise MQAError("mqa_decode", rc)
+            raise MQAError("mqa_decode_ex", rc)
         return self.out

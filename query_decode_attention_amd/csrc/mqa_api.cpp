@@ -75,7 +75,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MQA_OK : MQA_ERR_LAUN
 
 extern "C" {
 
-int mqa_abi_version(void) { return 100; }
+int mqa_abi_version(void) { return 200; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -117,23 +117,20 @@ size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache) {
   return mqa::decode_workspace_bytes(cache->b, h, cache->G, cache->d_h, cache->m_cap);
 }
 
-int mqa_decode(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens, float scale,
-               int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream) {
-  return mqa_decode_timed(q, h, cache, lens, scale, window, o, workspace, ws_bytes, stream,
-                          nullptr, nullptr);
-}
-
-int mqa_decode_timed(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens,
-                     float scale, int32_t window, void* o, void* workspace, size_t ws_bytes,
-                     void* stream, void* ev_begin, void* ev_end) {
+int mqa_decode_ex(const void* q, const void* k_new, const void* v_new, int32_t h,
+                  const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                  int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream,
+                  void* ev_begin, void* ev_end) {
   int rc = check_cache(cache);
   if (rc != MQA_OK) return rc;
   rc = check_heads(h, cache->G);
   if (rc != MQA_OK) return rc;
   if (window < 0) return MQA_ERR_SHAPE;
+  if ((k_new == nullptr) != (v_new == nullptr)) return MQA_ERR_NULL;
   if (cache->b == 0) return MQA_OK;
   if (!q || !o || !lens) return MQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return MQA_ERR_ALIGN;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return MQA_ERR_ALIGN;
   const size_t need = mqa::decode_workspace_bytes(cache->b, h, cache->G, cache->d_h, cache->m_cap);
   if (!workspace || !aligned16(workspace) || ws_bytes < need) return MQA_ERR_WORKSPACE;
   mqa::DecodeParams p;
@@ -141,6 +138,9 @@ int mqa_decode_timed(const void* q, int32_t h, const mqa_cache* cache, const int
   p.k = cache->k;
   p.v = cache->v;
   p.lens = lens;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.err_flag = err_flag;
   p.o = o;
   p.ws = workspace;
   p.b = cache->b;
@@ -154,6 +154,20 @@ int mqa_decode_timed(const void* q, int32_t h, const mqa_cache* cache, const int
   p.ev_begin = static_cast<hipEvent_t>(ev_begin);
   p.ev_end = static_cast<hipEvent_t>(ev_end);
   return launch_status(mqa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int mqa_decode(const void* q, int32_t h, const mqa_cache* cache, const int32_t* lens, float scale,
+               int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  return mqa_decode_ex(q, nullptr, nullptr, h, cache, const_cast<int32_t*>(lens), nullptr, scale,
+                       window, o, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+int mqa_append_decode(const void* q, const void* k_new, const void* v_new, int32_t h,
+                      const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                      int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  if (cache && cache->b > 0 && (!k_new || !v_new)) return MQA_ERR_NULL;
+  return mqa_decode_ex(q, k_new, v_new, h, cache, lens, err_flag, scale, window, o, workspace,
+                       ws_bytes, stream, nullptr, nullptr);
 }
 
 int mqa_prefill_causal(const void* Q, const void* K, const void* V, int32_t b, int32_t n,

@@ -1,30 +1,47 @@
-// mqa_decode.hip -- gfx950 kernels of one MQA/GQA decode step:
-//   kv_append_kernel      : concat of one new K/V row per sequence
-//                           (paper review, section 3 incremental pseudocode)
-//   decode_split_kernel   : scores, online softmax and weighted V over a
-//                           balanced share of all cached positions
-//                           (study notes section 4: o_i = softmax(q_i K^T s) V)
-//   decode_combine_kernel : exact merge of the split-K partial softmaxes
+// mqa_decode.hip -- gfx950 kernels of one MQA/GQA decode step.
+//
+//   kv_append_kernel : the incremental concat of one new K/V row per sequence
+//                      (paper review, section 3 multi-query pseudocode:
+//                      new_K = concat(prev_K, k)), for callers that append
+//                      separately.
+//   decode_kernel    : optionally the append, then scores, online softmax and
+//                      weighted V over every cached position (study notes
+//                      section 4: o_i = softmax(q_i K^T * scale) V).
+//   combine_kernel   : the exact merge of split segments, and the lens bump
+//                      of a fused append.
 //
 // Work decomposition.  The visible positions of every (sequence b, group g)
 // are cut into tiles of 32.  All tiles of all segments form one flat list of
-// T tiles; workgroup w of a grid of W takes tiles [T*w/W, T*(w+1)/W), so
-// every workgroup streams the same number of bytes whatever the length mix.
-// Inside a workgroup, wave k takes every NW-th tile of a segment; waves merge
-// their (max, sum, accumulator) through LDS; a segment that one workgroup
-// covers completely is normalised and written directly, the (at most two)
-// segments it shares with neighbours become fp32 partial records that the
-// combine kernel merges.  The flat tile list is derived on the device from
-// lens, so no host synchronisation is needed.
+// T tiles; workgroup w of a grid of W takes tiles [T*w/W, T*(w+1)/W), so every
+// workgroup streams the same number of bytes whatever the length mix.  Each
+// wave derives this schedule from lens by itself (wave-wide scan), so no host
+// synchronisation and no workgroup barrier precede the first K/V loads.
+//
+// Inside a workgroup, wave k takes every NW-th tile of a segment.  At the end
+// of a segment all waves park their (max, sum, accumulator) in LDS and the
+// workgroup folds them in a fixed order.  A segment that one workgroup covers
+// completely is normalised and written; a segment shared with neighbouring
+// workgroups becomes an fp32 partial record that the combine kernel merges.
+// The records cross from one workgroup to another only through the kernel
+// boundary: publishing them inside the kernel would need an agent-scope
+// release per workgroup, i.e. a write-back of an XCD's whole L2, which costs
+// far more on gfx950 than a second small launch.
+//
+// Fused append.  With k_new/v_new, sequence b attends over L_old + 1
+// positions; the row at L_old is read from k_new/v_new (never from the cache)
+// and the wave that owns it stores it into the cache.  lens itself is bumped
+// by the combine kernel, after every decode workgroup has read it.
 //
 // One wave, one 32-position tile, all h/G <= 32 heads of the group:
 //   S^T[32 pos][32 heads] = K_tile . Q^T        (MFMA; K rows are the A operand
 //                                                loaded straight from HBM)
 //   online softmax per head column (log2 domain, scale*log2(e) folded in)
-//   V_tile^T via an exact 0/1-selection MFMA    (turns position-major rows into
-//                                                the d-major A operand of PV)
+//   V_tile^T via an exact 0/1-selection MFMA    (position-major rows become the
+//                                                d-major A operand of PV)
 //   O^T[d][heads] += V^T . P^T                   (MFMA; P stays in registers)
 // Each K/V byte is read from HBM once and used by every head of its group.
+#include <stdlib.h>
+
 #include "mqa_device.h"
 #include "mqa_internal.h"
 
@@ -57,30 +74,47 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------- decode: shared ----
+// ------------------------------------------------------------ decode: args ----
 
-struct SplitArgs {
+struct DecodeArgs {
   const char* q;
-  const char* k;
-  const char* v;
-  const int32_t* lens;
+  char* k;               // cache; written only at the appended row
+  char* v;
+  int32_t* lens;         // read; +1 at the end of the kernel when appending
+  const char* k_new;     // nullable: no fused append
+  const char* v_new;
+  int32_t* err_flag;     // nullable
   char* o;
-  int32_t* prefix;  // [b + 1] exclusive prefix of tiles per sequence (written by block 0)
-  float* records;   // [2 * grid][rec_floats]
+  float* records;        // [2 * grid][rec_floats] partial results
+  int32_t* prefix;       // [b + 1] tiles before each sequence (written by workgroup 0)
   int b, h, G, hg, m_cap, window;
   int rec_floats;
   float scale_log2;
 };
 
-__device__ __forceinline__ void visible_range(const int32_t* lens, int bi, int m_cap, int window,
-                                              int& j0, int& L) {
-  int l = lens[bi];
-  l = l < 0 ? 0 : (l > m_cap ? m_cap : l);
-  j0 = (window > 0 && l > window) ? l - window : 0;
-  L = l;
+// Visible range [j0, L) of sequence bi and the appended position (or -1).
+struct SeqView {
+  int j0, L, app_pos;
+};
+
+__device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
+  const int raw = a.lens[bi];
+  int l = raw < 0 ? 0 : (raw > a.m_cap ? a.m_cap : raw);
+  int app = -1;
+  if (a.k_new && raw >= 0 && raw < a.m_cap) {
+    app = raw;
+    l = raw + 1;
+  }
+  SeqView s;
+  s.L = l;
+  s.j0 = (a.window > 0 && l > a.window) ? l - a.window : 0;
+  s.app_pos = app;
+  return s;
 }
 
-__device__ __forceinline__ int tiles_of(int j0, int L) { return (L - j0 + kTileRows - 1) / kTileRows; }
+__device__ __forceinline__ int tiles_of(const SeqView& s) {
+  return (s.L - s.j0 + kTileRows - 1) / kTileRows;
+}
 
 // First flat tile of workgroup w out of W over T tiles.
 __device__ __forceinline__ int64_t wg_start(int64_t T, int w, int W) { return T * w / W; }
@@ -89,31 +123,16 @@ __device__ __forceinline__ int wg_of(int64_t t, int64_t T, int W) {
   return (int)(((t + 1) * W + T - 1) / T) - 1;
 }
 
-// Exclusive block-wide prefix sum of v; `total` receives the block sum.
-template <int NW>
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
-  if (lane == 63) s_tmp[wave] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = s_tmp[w];
-    base += (w < wave) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  total = tot;
-  return base + x - v;
+  return x;
 }
 
-// ------------------------------------------------------ decode: split kernel ----
+// ------------------------------------------------------------ decode: tiles ----
 
 template <int NQ, bool FULL>
 __device__ __forceinline__ void load_kv(const char* kp, const char* vp, bool valid, int half,
@@ -125,6 +144,8 @@ __device__ __forceinline__ void load_kv(const char* kp, const char* vp, bool val
 #pragma unroll
     for (int c = 0; c < NQ; ++c)
       vr[c] = *reinterpret_cast<const u32x4*>(vp + (2 * c + half) * 16);
+    // issue every load of the tile before any use: one memory round trip
+    __builtin_amdgcn_sched_barrier(0);
   } else {
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
@@ -140,12 +161,15 @@ template <typename T, int DH, bool FULL>
 __device__ __forceinline__ void tile_update(WaveState<TileShape<T, DH>::ND>& st,
                                             const u32x4 (&kr)[TileShape<T, DH>::NQ],
                                             const u32x4 (&vr)[TileShape<T, DH>::NQ],
-                                            const u32x4 (&qr)[TileShape<T, DH>::NQ],
+                                            const u32x4 (*s_q)[64], int lane,
                                             const SelOps<T>& sel, float scale_log2,
                                             int pos0, int L, int half) {
   constexpr int NQ = TileShape<T, DH>::NQ;
   constexpr int ND = TileShape<T, DH>::ND;
   constexpr int VTC = TileShape<T, DH>::VTC;
+  u32x4 qr[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) qr[c] = s_q[c][lane];
   const f32x16 s = tile_scores<T, NQ>(kr, qr);
   float p[16];
   softmax_tile<T, ND, FULL>(st, s, scale_log2, pos0, L - 1, half, p);
@@ -159,34 +183,19 @@ __device__ __forceinline__ void tile_update(WaveState<TileShape<T, DH>::ND>& st,
   }
 }
 
+// ----------------------------------------------------------- decode: merging ----
+
+// LDS image of one wave's state, laid out so that lane i of every wave writes
+// and reads consecutive 16-byte words (bank-conflict free).
 template <int ND>
-struct MergeSlot {
+struct WaveSlot {
   f32x4 o[ND][4][64];
   float m[64];
   float l[64];
 };
 
-// Fold `other` (m_o, l_o, o_o) into `st` (exact softmax re-association).
 template <int ND>
-__device__ __forceinline__ void merge_into(WaveState<ND>& st, const MergeSlot<ND>& sl, int lane) {
-  const float m_o = sl.m[lane], l_o = sl.l[lane];
-  const float M = fmaxf(st.m, m_o);
-  const float Ms = (M == kNegInf) ? 0.f : M;  // both empty: keep zeros, avoid inf - inf
-  const float fa = fast_exp2(st.m - Ms), fb = fast_exp2(m_o - Ms);
-#pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 x = sl.o[d][r4][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.o[d][4 * r4 + i] = st.o[d][4 * r4 + i] * fa + x[i] * fb;
-    }
-  st.l = st.l * fa + l_o * fb;
-  st.m = M;
-}
-
-template <int ND>
-__device__ __forceinline__ void store_slot(const WaveState<ND>& st, MergeSlot<ND>& sl, int lane) {
+__device__ __forceinline__ void park(const WaveState<ND>& st, WaveSlot<ND>& sl, int lane) {
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -197,77 +206,95 @@ __device__ __forceinline__ void store_slot(const WaveState<ND>& st, MergeSlot<ND
   sl.l[lane] = st.l;
 }
 
-template <typename T, int DH, int NW, bool PREFETCH>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
+// Word e of a slot is (d block, r4, lane): head = lane % 32 and
+// d = 32*blk + 8*r4 + 4*(lane/32) .. +3.
+struct SlotIndex {
+  int blk, r4, lane;
+  __device__ __forceinline__ explicit SlotIndex(int e) {
+    lane = e & 63;
+    r4 = (e >> 6) & 3;
+    blk = e >> 8;
+  }
+  __device__ __forceinline__ int head() const { return lane & 31; }
+  __device__ __forceinline__ int d() const { return 32 * blk + 8 * r4 + 4 * (lane >> 5); }
+};
+
+// ------------------------------------------------------------ decode: kernel ----
+
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
-  static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "tree merge assumes NW a power of two <= 8");
-  __shared__ int s_scan[NW];
-  __shared__ int s_found[2];
-  __shared__ MergeSlot<ND> s_slot[NW > 1 ? NW / 2 : 1];
+  constexpr int kWords = ND * 4 * 64;  // f32x4 words per slot
+  __shared__ WaveSlot<ND> s_slot[NW];
+  __shared__ u32x4 s_q[NQ][64];        // Q^T operand of the current segment
+  __shared__ float s_fold[2][32];      // per-head max and sum of the folded state
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 31, half = lane >> 5;
+  const int W = gridDim.x;
 
-  // ---- schedule: tiles per sequence, total, and this workgroup's range ----
+  // ---- schedule (each wave on its own) ----
   int total = 0;
-  for (int c = 0; c < a.b; c += NW * 64) {
-    const int bi = c + (int)threadIdx.x;
+  for (int c = 0; c < a.b; c += 64) {
     int v = 0;
-    if (bi < a.b) {
-      int j0, L;
-      visible_range(a.lens, bi, a.m_cap, a.window, j0, L);
-      v = tiles_of(j0, L);
-    }
-    int tot;
-    const int ex = block_excl_scan<NW>(v, s_scan, tot);
-    if (blockIdx.x == 0 && bi < a.b) a.prefix[bi] = total + ex;
-    total += tot;
+    if (c + lane < a.b) v = tiles_of(seq_view(a, c + lane));
+    const int incl = wave_incl_scan(v, lane);
+    if (blockIdx.x == 0 && wave == 0 && c + lane < a.b) a.prefix[c + lane] = total + incl - v;
+    total += __shfl(incl, 63, 64);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) a.prefix[a.b] = total;
+  total = __builtin_amdgcn_readfirstlane(total);
   const int64_t Tt = (int64_t)total * a.G;
-  const int W = gridDim.x;
   const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
-  if (t0 >= t1) return;
 
-  // locate the sequence holding flat tile t0
-  if (threadIdx.x == 0) s_found[0] = -1;
-  __syncthreads();
-  int run = 0;
-  for (int c = 0; c < a.b; c += NW * 64) {
-    const int bi = c + (int)threadIdx.x;
-    int v = 0;
-    if (bi < a.b) {
-      int j0, L;
-      visible_range(a.lens, bi, a.m_cap, a.window, j0, L);
-      v = tiles_of(j0, L);
+  int b_cur = a.b;
+  int64_t seg_base = 0;
+  if (t0 < t1) {
+    int run = 0;
+    for (int c = 0; c < a.b; c += 64) {
+      int v = 0;
+      if (c + lane < a.b) v = tiles_of(seq_view(a, c + lane));
+      const int incl = wave_incl_scan(v, lane);
+      const int64_t lo = (int64_t)(run + incl - v) * a.G, hi = (int64_t)(run + incl) * a.G;
+      const uint64_t hit = __ballot(c + lane < a.b && v > 0 && lo <= t0 && t0 < hi);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        b_cur = c + src;
+        seg_base = (int64_t)(run + __shfl(incl - v, src, 64)) * a.G;
+        break;
+      }
+      run += __shfl(incl, 63, 64);
     }
-    int tot;
-    const int ex = block_excl_scan<NW>(v, s_scan, tot);
-    const int64_t lo = (int64_t)(run + ex) * a.G, hi = (int64_t)(run + ex + v) * a.G;
-    if (bi < a.b && v > 0 && lo <= t0 && t0 < hi) {
-      s_found[0] = bi;
-      s_found[1] = run + ex;
-    }
-    run += tot;
-    __syncthreads();
-    if (s_found[0] >= 0) break;
+    b_cur = __builtin_amdgcn_readfirstlane(b_cur);
   }
-  int b_cur = __builtin_amdgcn_readfirstlane(s_found[0]);
-  int64_t seg_base = (int64_t)__builtin_amdgcn_readfirstlane(s_found[1]) * a.G;
+
+  // Sequences with nothing visible get zeros; wave k of workgroup 0 checks
+  // sequences k*64 .. k*64+63, NW*64 at a time, and writes their rows.
+  if (blockIdx.x == 0) {
+    for (int c = wave * 64; c < a.b; c += NW * 64) {
+      uint64_t empty = __ballot(c + lane < a.b && tiles_of(seq_view(a, c + lane)) == 0);
+      while (empty) {
+        const int bi = c + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        T* op = reinterpret_cast<T*>(a.o) + (size_t)bi * a.h * DH;
+        for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
 
   SelOps<T> sel;
   sel.init(row, half);
-
   const size_t row_stride = (size_t)a.G * DH * sizeof(T);
   int64_t t = t0;
   bool first = true;
+
   while (t < t1 && b_cur < a.b) {
-    int j0, L;
-    visible_range(a.lens, b_cur, a.m_cap, a.window, j0, L);
-    j0 = __builtin_amdgcn_readfirstlane(j0);
-    L = __builtin_amdgcn_readfirstlane(L);
-    const int nb = tiles_of(j0, L);
+    const SeqView sv = seq_view(a, b_cur);
+    const int j0 = __builtin_amdgcn_readfirstlane(sv.j0);
+    const int L = __builtin_amdgcn_readfirstlane(sv.L);
+    const int app_pos = __builtin_amdgcn_readfirstlane(sv.app_pos);
+    const int nb = (L - j0 + kTileRows - 1) / kTileRows;
     if (nb == 0) {
       ++b_cur;
       continue;
@@ -277,105 +304,97 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
     const int ta = (int)(t - seg0);
     const int te = (int)((t1 < seg0 + nb ? t1 : seg0 + nb) - seg0);
     const bool complete = (ta == 0 && te == nb);
+    const int seg = b_cur * a.G + g;
 
-    // ---- per-wave pass over tiles ta + wave, ta + wave + NW, ... < te ----
+    // ---- this wave's tiles: ta + wave, ta + wave + NW, ... < te ----
     WaveState<ND> st;
     st.reset();
-    const int head = row;
-    u32x4 qr[NQ];
-    if (head < a.hg) {
-      const char* qp = a.q + ((size_t)b_cur * a.h + (size_t)g * a.hg + head) * DH * sizeof(T);
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) qr[c] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) qr[c] = u32x4{0u, 0u, 0u, 0u};
+    // Q^T operand of the group, staged once in LDS in lane order (chunk c of
+    // lane l is head l % 32, 16-byte chunk 2c + l / 32 of its row).
+    {
+      const char* qp = a.q + ((size_t)b_cur * a.h + (size_t)g * a.hg + row) * DH * sizeof(T);
+      for (int c = wave; c < NQ; c += NW) {
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (row < a.hg) x = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+        s_q[c][lane] = x;
+      }
     }
+    __syncthreads();
     const size_t seq_off = ((size_t)b_cur * a.m_cap * a.G + (size_t)g) * DH * sizeof(T);
-    const char* kseq = a.k + seq_off;
-    const char* vseq = a.v + seq_off;
+    const size_t new_off = ((size_t)b_cur * a.G + (size_t)g) * DH * sizeof(T);
 
-    auto tile_ptrs = [&](int tile, const char*& kp, const char*& vp, int& pos0) {
-      pos0 = j0 + tile * kTileRows;
-      const size_t off = (size_t)(pos0 + row) * row_stride;
-      kp = kseq + off;
-      vp = vseq + off;
-    };
-    auto run_tile = [&](int tile, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
+    for (int tile = ta + wave; tile < te; tile += NW) {
       const int pos0 = j0 + tile * kTileRows;
-      if (pos0 + kTileRows <= L)
-        tile_update<T, DH, true>(st, kr, vr, qr, sel, a.scale_log2, pos0, L, half);
-      else
-        tile_update<T, DH, false>(st, kr, vr, qr, sel, a.scale_log2, pos0, L, half);
-    };
-    auto load_tile = [&](int tile, u32x4 (&kr)[NQ], u32x4 (&vr)[NQ]) {
-      const char *kp, *vp;
-      int pos0;
-      tile_ptrs(tile, kp, vp, pos0);
-      if (pos0 + kTileRows <= L)
-        load_kv<NQ, true>(kp, vp, true, half, kr, vr);
-      else
-        load_kv<NQ, false>(kp, vp, pos0 + row < L, half, kr, vr);
-    };
-
-    int tile = ta + wave;
-    if constexpr (PREFETCH) {
-      u32x4 kA[NQ], vA[NQ], kB[NQ], vB[NQ];
-      if (tile < te) load_tile(tile, kA, vA);
-      while (tile < te) {
-        if (tile + NW < te) load_tile(tile + NW, kB, vB);
-        run_tile(tile, kA, vA);
-        tile += NW;
-        if (tile >= te) break;
-        if (tile + NW < te) load_tile(tile + NW, kA, vA);
-        run_tile(tile, kB, vB);
-        tile += NW;
-      }
-    } else {
-      u32x4 kA[NQ], vA[NQ];
-      for (; tile < te; tile += NW) {
-        load_tile(tile, kA, vA);
-        run_tile(tile, kA, vA);
-      }
-    }
-
-    // ---- merge the waves (tree through LDS) ----
-#pragma unroll
-    for (int s = NW / 2; s >= 1; s /= 2) {
-      if (wave >= s && wave < 2 * s) store_slot<ND>(st, s_slot[wave - s], lane);
-      __syncthreads();
-      if (wave < s) merge_into<ND>(st, s_slot[wave], lane);
-      __syncthreads();
-    }
-
-    // ---- wave 0 writes the segment result ----
-    const float l_tot = st.l + xor32(st.l);
-    if (wave == 0 && head < a.hg) {
-      if (complete) {
-        const float inv = 1.0f / l_tot;
-        T* op = reinterpret_cast<T*>(a.o) + ((size_t)b_cur * a.h + (size_t)g * a.hg + head) * DH;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            store4(op + 32 * d + 8 * r4 + 4 * half, st.o[d][4 * r4] * inv,
-                   st.o[d][4 * r4 + 1] * inv, st.o[d][4 * r4 + 2] * inv,
-                   st.o[d][4 * r4 + 3] * inv);
+      const int pos = pos0 + row;
+      u32x4 kr[NQ], vr[NQ];
+      if (pos0 + kTileRows <= L && app_pos < pos0) {
+        const size_t off = seq_off + (size_t)pos * row_stride;
+        load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
+        tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
       } else {
-        float* rec = a.records + ((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * a.rec_floats;
-        float* ro = rec + (size_t)head * DH;
+        // last tile of the segment: ragged, and/or holding the appended row
+        const bool is_new = (pos == app_pos);
+        const char* kp = is_new ? a.k_new + new_off : a.k + seq_off + (size_t)pos * row_stride;
+        const char* vp = is_new ? a.v_new + new_off : a.v + seq_off + (size_t)pos * row_stride;
+        load_kv<NQ, false>(kp, vp, pos < L, half, kr, vr);
+        if (is_new) {  // the concat: store the new row into the cache
+          char* kc = a.k + seq_off + (size_t)pos * row_stride;
+          char* vc = a.v + seq_off + (size_t)pos * row_stride;
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+          for (int c = 0; c < NQ; ++c) {
+            *reinterpret_cast<u32x4*>(kc + (2 * c + half) * 16) = kr[c];
+            *reinterpret_cast<u32x4*>(vc + (2 * c + half) * 16) = vr[c];
+          }
+        }
+        if (pos0 + kTileRows <= L)
+          tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+        else
+          tile_update<T, DH, false>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+      }
+    }
+
+    // ---- fold the waves: park in LDS, combine in a fixed order ----
+    park<ND>(st, s_slot[wave], lane);
+    __syncthreads();
+    if (threadIdx.x < 32) {  // per-head max and sum over the waves
+      const int hd = threadIdx.x;
+      float M = kNegInf;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            store4(ro + 32 * d + 8 * r4 + 4 * half, st.o[d][4 * r4], st.o[d][4 * r4 + 1],
-                   st.o[d][4 * r4 + 2], st.o[d][4 * r4 + 3]);
-        if (half == 0) {
-          rec[(size_t)a.hg * DH + head] = st.m;
-          rec[(size_t)a.hg * DH + a.hg + head] = l_tot;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_slot[w].m[hd]);
+      const float Ms = (M == kNegInf) ? 0.f : M;
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        l += (s_slot[w].l[hd] + s_slot[w].l[hd + 32]) * fast_exp2(s_slot[w].m[hd] - Ms);
+      s_fold[0][hd] = M;
+      s_fold[1][hd] = l;
+    }
+    __syncthreads();
+    float* rec = a.records + ((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * a.rec_floats;
+    for (int e = threadIdx.x; e < kWords; e += NW * 64) {
+      const SlotIndex ix(e);
+      const int hd = ix.head();
+      if (hd >= a.hg) continue;
+      const float M = s_fold[0][hd];
+      const float Ms = (M == kNegInf) ? 0.f : M;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        acc += s_slot[w].o[ix.blk][ix.r4][ix.lane] * fast_exp2(s_slot[w].m[hd] - Ms);
+      if (complete) {
+        const float inv = 1.0f / s_fold[1][hd];
+        T* op = reinterpret_cast<T*>(a.o) + ((size_t)b_cur * a.h + (size_t)g * a.hg + hd) * DH + ix.d();
+        store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      } else {
+        *reinterpret_cast<f32x4*>(rec + (size_t)hd * DH + ix.d()) = acc;
+        if (ix.blk == 0 && ix.r4 == 0 && ix.lane < 32) {
+          rec[(size_t)a.hg * DH + hd] = M;
+          rec[(size_t)a.hg * DH + a.hg + hd] = s_fold[1][hd];
         }
       }
     }
+
+    __syncthreads();  // LDS slots are reused by the next segment
 
     first = false;
     t = seg0 + te;
@@ -384,59 +403,127 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
       ++b_cur;
     }
   }
+
 }
 
-// --------------------------------------------------- decode: combine kernel ----
+// --------------------------------------------------------- combine kernel ----
 
 struct CombineArgs {
-  const int32_t* lens;
   const int32_t* prefix;
   const float* records;
+  int32_t* lens;         // bumped when the decode appended
+  int32_t* err_flag;     // nullable
   char* o;
-  int b, h, G, hg, m_cap, window, rec_floats, grid;
+  int b, h, G, hg, m_cap, rec_floats, grid;
+  int append;
 };
 
+// Merge of the partial records of one (sequence, group) segment:
+// M = max_k m_k, weights f_k = exp2(m_k - M), o = sum_k f_k acc_k / sum_k f_k l_k
+// (the softmax re-associated exactly).  The per-record weights go through LDS
+// so that the loads of the final sum are independent of each other.
+// Block (seg, y) handles the heads [y*HPB, (y+1)*HPB) of segment seg.
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int kD4 = DH / 4;            // float4 words per head row
+  constexpr int HPB = 256 / kD4;         // heads per block
+  constexpr int kMaxRec = 128;           // records held in LDS per pass
+  __shared__ float s_f[kMaxRec][HPB];
+  __shared__ float s_inv[HPB];
+  __shared__ int s_rec[kMaxRec];
+
+  if (a.append && blockIdx.x == 0 && blockIdx.y == 0) {
+    int over = 0;
+    for (int bi = threadIdx.x; bi < a.b; bi += 256) {
+      const int raw = a.lens[bi];
+      if (raw >= 0 && raw < a.m_cap) a.lens[bi] = raw + 1;
+      else over = 1;
+    }
+    if (over && a.err_flag) *a.err_flag = 1;
+  }
+
   const int seg = blockIdx.x;
   const int bi = seg / a.G, g = seg % a.G;
-  const int idx = blockIdx.y * 256 + threadIdx.x;
-  if (idx >= a.hg * (DH / 4)) return;
-  const int head = idx / (DH / 4), d4 = idx % (DH / 4);
-  T* out = reinterpret_cast<T*>(a.o) + ((size_t)bi * a.h + (size_t)g * a.hg + head) * DH + 4 * d4;
-  int j0, L;
-  visible_range(a.lens, bi, a.m_cap, a.window, j0, L);
-  const int nb = tiles_of(j0, L);
-  if (nb == 0) {  // empty row: zeros by convention
-    store4(out, 0.f, 0.f, 0.f, 0.f);
-    return;
-  }
+  const int nb = a.prefix[bi + 1] - a.prefix[bi];
+  if (nb == 0) return;
   const int64_t Tt = (int64_t)a.prefix[a.b] * a.G;
-  const int64_t S = (int64_t)a.prefix[bi] * a.G + (int64_t)g * nb;
-  const int wf = wg_of(S, Tt, a.grid), wl = wg_of(S + nb - 1, Tt, a.grid);
+  const int64_t S0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * nb;
+  const int wf = wg_of(S0, Tt, a.grid), wl = wg_of(S0 + nb - 1, Tt, a.grid);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
-  // Workgroups between wf and wl whose range is empty (grid > tiles) wrote
-  // nothing and are skipped.
-  float M = kNegInf;
-  for (int w = wf; w <= wl; ++w) {
-    if (wg_start(Tt, w, a.grid) == wg_start(Tt, w + 1, a.grid)) continue;
-    const int slot = (w == wf && wg_start(Tt, w, a.grid) < S) ? 1 : 0;
-    const float* rec = a.records + ((size_t)w * 2 + slot) * a.rec_floats;
-    M = fmaxf(M, rec[(size_t)a.hg * DH + head]);
-  }
+
+  const int hd0 = blockIdx.y * HPB;
+  const int hl = threadIdx.x / kD4, d4 = threadIdx.x % kD4;
+  const int hd = hd0 + hl;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  for (int w = wf; w <= wl; ++w) {
-    if (wg_start(Tt, w, a.grid) == wg_start(Tt, w + 1, a.grid)) continue;
-    const int slot = (w == wf && wg_start(Tt, w, a.grid) < S) ? 1 : 0;
-    const float* rec = a.records + ((size_t)w * 2 + slot) * a.rec_floats;
-    const float f = fast_exp2(rec[(size_t)a.hg * DH + head] - M);
-    lsum += f * rec[(size_t)a.hg * DH + a.hg + head];
-    const f32x4 x = *reinterpret_cast<const f32x4*>(rec + (size_t)head * DH + 4 * d4);
-    acc += x * f;
+  float M = kNegInf, lsum = 0.f;        // running (per head, kept by thread d4 == 0)
+  // walk the contributing workgroups kMaxRec at a time
+  for (int w0 = wf; w0 <= wl; w0 += kMaxRec) {
+    const int w1 = min(wl, w0 + kMaxRec - 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int n = 0;
+      for (int w = w0; w <= w1; ++w) {
+        if (wg_start(Tt, w, a.grid) == wg_start(Tt, w + 1, a.grid)) { s_rec[n++] = -1; continue; }
+        const int slot = (w == wf && wg_start(Tt, w, a.grid) < S0) ? 1 : 0;
+        s_rec[n++] = w * 2 + slot;
+      }
+    }
+    __syncthreads();
+    const int n = w1 - w0 + 1;
+    for (int e = threadIdx.x; e < n * HPB; e += 256) {
+      const int k = e / HPB, h2 = e % HPB;
+      float m = kNegInf;
+      if (s_rec[k] >= 0 && hd0 + h2 < a.hg)
+        m = a.records[(size_t)s_rec[k] * a.rec_floats + (size_t)a.hg * DH + hd0 + h2];
+      s_f[k][h2] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < HPB && hd0 + threadIdx.x < a.hg) {
+      const int h2 = threadIdx.x;
+      float Mn = M;
+      for (int k = 0; k < n; ++k) Mn = fmaxf(Mn, s_f[k][h2]);
+      const float Ms = (Mn == kNegInf) ? 0.f : Mn;
+      float l = lsum * fast_exp2(M - Ms);
+      for (int k = 0; k < n; ++k) {
+        const float f = fast_exp2(s_f[k][h2] - Ms);
+        s_f[k][h2] = f;
+        if (s_rec[k] >= 0)
+          l += f * a.records[(size_t)s_rec[k] * a.rec_floats + (size_t)a.hg * DH + a.hg + hd0 + h2];
+      }
+      s_inv[h2] = fast_exp2(M - Ms);  // rescale of the running sum of earlier passes
+      M = Mn;
+      lsum = l;
+    }
+    __syncthreads();
+    if (hd < a.hg) {
+      acc *= s_inv[hl];
+      int k = 0;
+      for (; k + 4 <= n; k += 4) {
+        f32x4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (s_rec[k + u] >= 0)
+            x[u] = *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[k + u] * a.rec_floats +
+                                                   (size_t)hd * DH + 4 * d4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += x[u] * s_f[k + u][hl];
+      }
+      for (; k < n; ++k)
+        if (s_rec[k] >= 0)
+          acc += *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[k] * a.rec_floats +
+                                                 (size_t)hd * DH + 4 * d4) * s_f[k][hl];
+    }
   }
-  const float inv = 1.0f / lsum;
-  store4(out, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  __syncthreads();
+  if (threadIdx.x < HPB) s_inv[threadIdx.x] = 1.0f / lsum;
+  __syncthreads();
+  if (hd < a.hg) {
+    const float inv = s_inv[hl];
+    T* op = reinterpret_cast<T*>(a.o) + ((size_t)bi * a.h + (size_t)g * a.hg + hd) * DH + 4 * d4;
+    store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  }
 }
 
 // ------------------------------------------------------------------- host ----
@@ -447,6 +534,7 @@ size_t decode_record_bytes(int hg, int dh) {
   return f * sizeof(float);
 }
 
+// Schedule header: the [b + 1] tile prefix, padded to 256 bytes.
 size_t decode_records_offset(int b) {
   return (((size_t)b + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
@@ -466,66 +554,75 @@ constexpr int kDecodeWaves = 8;
 
 template <typename T, int DH>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  constexpr bool kPrefetch = false;
-  auto split = decode_split_kernel<T, DH, kDecodeWaves, kPrefetch>;
+  auto kern = decode_kernel<T, DH, kDecodeWaves>;
   int dev = 0;
   const int cus = current_device_cus(&dev);
   if (cus <= 0) return hipErrorInvalidDevice;
-  // Occupancy of the split kernel, cached per device.
   static int occ_cache[64];
   int occ = (dev >= 0 && dev < 64) ? occ_cache[dev] : 0;
   if (occ <= 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, split, kDecodeWaves * 64, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kDecodeWaves * 64, 0);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
     if (dev >= 0 && dev < 64) occ_cache[dev] = occ;
   }
   int grid = cus * occ;
+  // Tuning override of the grid (workgroups); never above the cap.
+  static const int grid_env = [] {
+    const char* e = getenv("MQA_DECODE_GRID");
+    return e ? atoi(e) : 0;
+  }();
+  if (grid_env > 0) grid = grid_env;
   const int cap = decode_grid_cap(p.b, p.G, p.m_cap);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
 
-  SplitArgs sa;
-  sa.q = (const char*)p.q;
-  sa.k = (const char*)p.k;
-  sa.v = (const char*)p.v;
-  sa.lens = p.lens;
-  sa.o = (char*)p.o;
-  sa.prefix = (int32_t*)p.ws;
-  sa.records = (float*)((char*)p.ws + decode_records_offset(p.b));
-  sa.b = p.b;
-  sa.h = p.h;
-  sa.G = p.G;
-  sa.hg = p.h / p.G;
-  sa.m_cap = p.m_cap;
-  sa.window = p.window;
-  sa.rec_floats = (int)(decode_record_bytes(sa.hg, DH) / sizeof(float));
-  sa.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  DecodeArgs a;
+  a.q = (const char*)p.q;
+  a.k = (char*)p.k;
+  a.v = (char*)p.v;
+  a.lens = const_cast<int32_t*>(p.lens);
+  a.k_new = (const char*)p.k_new;
+  a.v_new = (const char*)p.v_new;
+  a.err_flag = p.err_flag;
+  a.o = (char*)p.o;
+  a.prefix = (int32_t*)p.ws;
+  a.records = (float*)((char*)p.ws + decode_records_offset(p.b));
+  a.b = p.b;
+  a.h = p.h;
+  a.G = p.G;
+  a.hg = p.h / p.G;
+  a.m_cap = p.m_cap;
+  a.window = p.window;
+  a.rec_floats = (int)(decode_record_bytes(a.hg, DH) / sizeof(float));
+  a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
   hipError_t e;
   if (p.ev_begin && (e = hipEventRecord(p.ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(split, dim3(grid), dim3(kDecodeWaves * 64), 0, s, sa);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kDecodeWaves * 64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_end && (e = hipEventRecord(p.ev_end, s)) != hipSuccess) return e;
 
   CombineArgs ca;
-  ca.lens = p.lens;
-  ca.prefix = sa.prefix;
-  ca.records = sa.records;
-  ca.o = (char*)p.o;
+  ca.prefix = a.prefix;
+  ca.records = a.records;
+  ca.lens = a.lens;
+  ca.err_flag = a.err_flag;
+  ca.o = a.o;
   ca.b = p.b;
   ca.h = p.h;
   ca.G = p.G;
-  ca.hg = sa.hg;
+  ca.hg = a.hg;
   ca.m_cap = p.m_cap;
-  ca.window = p.window;
-  ca.rec_floats = sa.rec_floats;
+  ca.rec_floats = a.rec_floats;
   ca.grid = grid;
-  const int per_seg = sa.hg * (DH / 4);
-  dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((per_seg + 255) / 256));
-  hipLaunchKernelGGL((decode_combine_kernel<T, DH>), cgrid, dim3(256), 0, s, ca);
+  ca.append = p.k_new != nullptr;
+  constexpr int kHeadsPerBlock = 256 / (DH / 4);
+  dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));
+  hipLaunchKernelGGL((combine_kernel<T, DH>), cgrid, dim3(256), 0, s, ca);
   return hipGetLastError();
 }
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

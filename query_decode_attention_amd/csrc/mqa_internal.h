@@ -17,7 +17,10 @@ struct DecodeParams {
   const void* q;
   const void* k;
   const void* v;
-  const int32_t* lens;
+  const int32_t* lens;     // written (+1) only when k_new is set
+  const void* k_new;       // nullable: fused append
+  const void* v_new;
+  int32_t* err_flag;       // nullable
   void* o;
   void* ws;
   int b, h, G, dh, m_cap, window, dtype;

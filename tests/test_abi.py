@@ -37,6 +37,8 @@ def lib(libmqa_path):
     L.mqa_decode_workspace_size.argtypes = [I32, CP]
     L.mqa_decode_workspace_size.restype = SZ
     L.mqa_decode.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P]
+    L.mqa_append_decode.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P]
+    L.mqa_decode_ex.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P]
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
     return L
@@ -52,8 +54,9 @@ def cache(b=2, m_cap=64, G=1, dh=128, dtype=1, k=FAKE, v=FAKE):
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
-        "mqa_abi_version", "mqa_check_lens", "mqa_decode", "mqa_decode_timed",
-        "mqa_decode_workspace_size", "mqa_kv_append", "mqa_prefill_causal", "mqa_strerror"])
+        "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
+        "mqa_decode_ex", "mqa_decode_workspace_size",
+        "mqa_kv_append", "mqa_prefill_causal", "mqa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib, libmqa_path):
@@ -69,7 +72,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 100
+    assert q.abi_version() == 200
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -83,6 +86,8 @@ def test_workspace_size_is_pure_host_arithmetic(lib):
     assert n == 512 + 2 * 2048 * (32 * 130 * 4)
     small = cache(b=1, m_cap=128, G=1, dh=64)
     assert f(4, ctypes.byref(small)) == 256 + 2 * 4 * ((4 * 66 + 3) // 4 * 4 * 4)
+    gqa = cache(b=32, m_cap=32768, G=8, dh=128)
+    assert f(64, ctypes.byref(gqa)) == 256 + 2 * 2048 * (8 * 130 * 4)
     assert f(3, ctypes.byref(cache(G=2))) == 0          # G does not divide h
     assert f(64, ctypes.byref(cache(G=1))) == 0         # h/G > 32
     assert f(4, ctypes.byref(cache(dh=96))) == 0        # d_h
@@ -113,6 +118,26 @@ def test_decode_rejects_bad_arguments_before_launching(lib):
     assert call(wsb=100) == EWS
     assert call(w=FAKE_MIS) == EWS
     assert call(c=cache(b=0)) == OK                     # nothing to do, nothing launched
+
+
+def test_fused_append_decode_rejects_bad_arguments(lib):
+    ad = lib.mqa_append_decode
+    c = cache()
+    ws = 1 << 30
+
+    def call(kn=FAKE, vn=FAKE, q=FAKE, lens=FAKE, w=FAKE, wsb=ws, c=c):
+        return ad(q, kn, vn, 4, ctypes.byref(c), lens, None, 1.0, 0, FAKE, w, wsb, None)
+
+    assert call(kn=None) == ENULL
+    assert call(vn=None) == ENULL
+    assert call(lens=None) == ENULL
+    assert call(kn=FAKE_MIS) == EALIGN
+    assert call(wsb=64) == EWS
+    assert call(c=cache(dh=48)) == EDHEAD
+    ex = lib.mqa_decode_ex
+    # exactly one of k_new / v_new given
+    assert ex(FAKE, FAKE, None, 4, ctypes.byref(c), FAKE, None, 1.0, 0, FAKE, FAKE, ws, None,
+              None, None) == ENULL
 
 
 def test_append_and_prefill_reject_bad_arguments(lib):

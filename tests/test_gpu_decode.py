@@ -20,12 +20,19 @@ def to_dev(d):
     return {k: v.cuda() for k, v in d.items()}
 
 
-def run_decode(inp, scale, window=0, append=False):
-    """Runs (optional append +) decode on the GPU; returns (o, K, V, lens) on device."""
+def run_decode(inp, scale, window=0, append=False, fused=True):
+    """Runs (optional append +) decode on the GPU; returns (o, device tensors).
+
+    fused=True appends inside the decode kernel (mqa_append_decode);
+    fused=False issues mqa_kv_append then mqa_decode."""
     d = to_dev(inp)
-    if append:
-        mqa.kv_append(d["k_new"], d["v_new"], d["K"], d["V"], d["lens"])
-    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], scale, window=window)
+    if append and fused:
+        o = mqa.append_decode(d["q"], d["k_new"], d["v_new"], d["K"], d["V"], d["lens"], scale,
+                              window=window)
+    else:
+        if append:
+            mqa.kv_append(d["k_new"], d["v_new"], d["K"], d["V"], d["lens"])
+        o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], scale, window=window)
     torch.cuda.synchronize()
     return o, d
 
@@ -72,12 +79,12 @@ def test_decode_parity_grid(case):
     assert_parity(o, ref, dtype, f"grid {case}")
 
 
-@pytest.mark.parametrize("append", [False, True])
-def test_decode_many_sequences_multi_chunk_scan(append):
-    """b > 256 exercises the multi-chunk device scan of the schedule."""
-    announce(f"decode b=600 append={append}")
+@pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
+def test_decode_many_sequences_multi_chunk_scan(append, fused):
+    """b > 64 exercises the multi-chunk wave scan of the schedule."""
+    announce(f"decode b=600 append={append} fused={fused}")
     cfg, inp = make(torch.bfloat16, 600, 8, 1, 64, 96, 0, 95, seed=7100 + append)
-    o, _ = run_decode(inp, cfg.scale, append=append)
+    o, _ = run_decode(inp, cfg.scale, append=append, fused=fused)
     ref, _ = oracle_step(inp, cfg.scale, append=append)
     assert_parity(o, ref, torch.bfloat16, "b=600")
 
@@ -112,14 +119,22 @@ def test_c2_full(cfg):
     assert_parity(o, ref, torch.bfloat16, cfg.name)
 
 
-def test_c3_serving_full_with_append():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-call"])
+def test_c3_serving_full_with_append(fused):
     """b=64, h=32, ragged lens U{1..8192} + one append, exactly as timed."""
-    announce("c3 full size (append + decode)")
+    announce(f"c3 full size (append + decode), fused={fused}")
     inp = W.decode_inputs(W.C3)
-    o, d = run_decode(inp, W.C3.scale, append=True)
+    o, d = run_decode(inp, W.C3.scale, append=True, fused=fused)
     ref, lens_ref = oracle_step(inp, W.C3.scale, append=True)
     assert np.array_equal(d["lens"].cpu().numpy(), lens_ref)
     assert_parity(o, ref, torch.bfloat16, "c3")
+    Kr, _ = oracle._raw(inp["K"])
+    Kr = Kr.copy()
+    Vr, _ = oracle._raw(inp["V"])
+    Vr = Vr.copy()
+    oracle.kv_append(inp["k_new"], inp["v_new"], Kr, Vr, inp["lens"].numpy().copy())
+    assert d["K"].cpu().view(torch.int16).numpy().view(np.uint16).tobytes() == Kr.tobytes()
+    assert d["V"].cpu().view(torch.int16).numpy().view(np.uint16).tobytes() == Vr.tobytes()
 
 
 def test_c4_gqa_full_sampled():
@@ -253,9 +268,11 @@ def test_append_is_bit_exact_and_flags_full_caches():
     mqa.check_lens(d["lens"][:4].contiguous(), 64)
 
 
-def test_serial_decode_loop_matches_oracle():
-    """Ten append+decode steps with a growing cache (the serial token loop)."""
-    announce("10-step loop")
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-call"])
+def test_serial_decode_loop_matches_oracle(fused):
+    """Ten append+decode steps with a growing cache (the serial token loop),
+    one workspace reused by every step."""
+    announce(f"10-step loop fused={fused}")
     cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 300, 20, 250, seed=7430)
     d = to_dev(inp)
     Kr, _ = oracle._raw(inp["K"])
@@ -268,11 +285,47 @@ def test_serial_decode_loop_matches_oracle():
         kn = torch.randn(4, 1, 128, generator=g).to(torch.bfloat16)
         vn = torch.randn(4, 1, 128, generator=g).to(torch.bfloat16)
         q = torch.randn(4, 32, 128, generator=g).to(torch.bfloat16)
-        mqa.kv_append(kn.cuda(), vn.cuda(), d["K"], d["V"], d["lens"])
-        o = mqa.decode(q.cuda(), d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
+        if fused:
+            o = mqa.append_decode(q.cuda(), kn.cuda(), vn.cuda(), d["K"], d["V"], d["lens"],
+                                  cfg.scale, workspace=ws)
+        else:
+            mqa.kv_append(kn.cuda(), vn.cuda(), d["K"], d["V"], d["lens"])
+            o = mqa.decode(q.cuda(), d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
         oracle.kv_append(kn, vn, Kr, Vr, lens)
         ref = oracle.decode(q, Kr, Vr, lens, cfg.scale)
         assert_parity(o, ref, torch.bfloat16, f"loop step {step}")
+
+
+def test_fused_append_full_caches_flag_and_keep_lens():
+    """Full caches get no new row in the fused path either: lens stays, the
+    flag is set, the sequence attends over its m_cap rows."""
+    announce("fused append with full caches")
+    cfg, inp = make(torch.bfloat16, 5, 32, 2, 128, 64, 0, 64, seed=7440)
+    inp["lens"] = torch.tensor([0, 63, 64, 10, 70], dtype=torch.int32)
+    d = to_dev(inp)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = mqa.append_decode(d["q"], d["k_new"], d["v_new"], d["K"], d["V"], d["lens"], cfg.scale,
+                          err_flag=err)
+    torch.cuda.synchronize()
+    ref, lens_ref = oracle_step(inp, cfg.scale, append=True)
+    assert err.item() == 1
+    assert d["lens"].cpu().tolist() == lens_ref.tolist() == [1, 64, 64, 11, 70]
+    assert_parity(o, ref, torch.bfloat16, "fused full caches")
+
+
+def test_decode_workspace_reused_across_shapes_of_lens():
+    """One workspace across calls whose lens mixes alternate between split
+    and unsplit segments: nothing stale leaks from one call to the next."""
+    announce("workspace reuse")
+    cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 3000, 1, 3000, seed=7450)
+    d = to_dev(inp)
+    ws = mqa.workspace_for(32, d["K"])
+    g = torch.Generator().manual_seed(3)
+    for it in range(6):
+        lens = torch.randint(0, 3001 if it % 2 else 40, (4,), generator=g).to(torch.int32)
+        o = mqa.decode(d["q"], d["K"], d["V"], lens.cuda(), cfg.scale, workspace=ws)
+        ref = oracle.decode(inp["q"], inp["K"], inp["V"], lens.numpy(), cfg.scale)
+        assert_parity(o, ref, torch.bfloat16, f"reuse {it}")
 
 
 # ------------------------------------------------------------------ errors
