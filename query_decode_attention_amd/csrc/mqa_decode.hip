@@ -86,7 +86,8 @@ struct DecodeArgs {
   int32_t* err_flag;     // nullable
   char* o;
   float* records;        // [2 * grid][rec_floats] partial results
-  int32_t* prefix;       // [b + 1] tiles before each sequence (written by workgroup 0)
+  int32_t* prefix;       // [b + 1] tiles before each sequence, then the count of
+                         // non-empty sequences (written by workgroup 0)
   int b, h, G, hg, m_cap, window;
   int rec_floats;
   float scale_log2;
@@ -114,6 +115,16 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
 
 __device__ __forceinline__ int tiles_of(const SeqView& s) {
   return (s.L - s.j0 + kTileRows - 1) / kTileRows;
+}
+
+// Workgroups that share the T tiles of `segs` non-empty segments: the
+// launched grid, but no more than one per `min_tiles` tiles unless there are
+// more segments than that (short segments are better run side by side than
+// one after another).  Both kernels derive the same value.
+__device__ __forceinline__ int effective_grid(int64_t T, int64_t segs, int grid, int min_tiles) {
+  int64_t w = (T + min_tiles - 1) / min_tiles;
+  if (w < segs) w = segs;
+  return (int)(w < 1 ? 1 : (w < grid ? w : grid));
 }
 
 // First flat tile of workgroup w out of W over T tiles.
@@ -219,6 +230,22 @@ struct SlotIndex {
   __device__ __forceinline__ int d() const { return 32 * blk + 8 * r4 + 4 * (lane >> 5); }
 };
 
+// Q^T operand of group g of sequence bi, staged once in LDS in lane order:
+// chunk c of lane l is head l % 32, 16-byte chunk 2c + l / 32 of its row
+// (zeros for heads >= h/G).
+template <typename T, int DH, int NW>
+__device__ __forceinline__ void stage_q(const DecodeArgs& a, u32x4 (*s_q)[64], int bi, int g,
+                                        int wave, int lane) {
+  constexpr int NQ = TileShape<T, DH>::NQ;
+  const int row = lane & 31, half = lane >> 5;
+  const char* qp = a.q + ((size_t)bi * a.h + (size_t)g * a.hg + row) * DH * sizeof(T);
+  for (int c = wave; c < NQ; c += NW) {
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (row < a.hg) x = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+    s_q[c][lane] = x;
+  }
+}
+
 // ------------------------------------------------------------ decode: kernel ----
 
 template <typename T, int DH, int NW>
@@ -232,20 +259,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 31, half = lane >> 5;
-  const int W = gridDim.x;
 
   // ---- schedule (each wave on its own) ----
-  int total = 0;
+  int total = 0, nonempty = 0;
   for (int c = 0; c < a.b; c += 64) {
     int v = 0;
     if (c + lane < a.b) v = tiles_of(seq_view(a, c + lane));
     const int incl = wave_incl_scan(v, lane);
     if (blockIdx.x == 0 && wave == 0 && c + lane < a.b) a.prefix[c + lane] = total + incl - v;
     total += __shfl(incl, 63, 64);
+    nonempty += __popcll(__ballot(v > 0));
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.prefix[a.b] = total;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.prefix[a.b] = total;
+    a.prefix[a.b + 1] = nonempty;
+  }
   total = __builtin_amdgcn_readfirstlane(total);
   const int64_t Tt = (int64_t)total * a.G;
+  // Workgroups in use (see effective_grid): every wave has work, short
+  // segments still run side by side.
+  const int W = effective_grid(Tt, (int64_t)nonempty * a.G, gridDim.x, NW);
   const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
 
   int b_cur = a.b;
@@ -306,50 +339,61 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const bool complete = (ta == 0 && te == nb);
     const int seg = b_cur * a.G + g;
 
-    // ---- this wave's tiles: ta + wave, ta + wave + NW, ... < te ----
-    WaveState<ND> st;
-    st.reset();
-    // Q^T operand of the group, staged once in LDS in lane order (chunk c of
-    // lane l is head l % 32, 16-byte chunk 2c + l / 32 of its row).
-    {
-      const char* qp = a.q + ((size_t)b_cur * a.h + (size_t)g * a.hg + row) * DH * sizeof(T);
-      for (int c = wave; c < NQ; c += NW) {
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (row < a.hg) x = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
-        s_q[c][lane] = x;
-      }
-    }
-    __syncthreads();
+    // ---- this wave's tiles ----
+    // Tiles go round-robin over the waves by their index in the workgroup's
+    // range (not in the segment), so a range that spans segments still gives
+    // every wave the same number of tiles, to within one.
+    const int rel0 = (int)(t - t0);  // workgroup-relative index of tile ta
+    int tile = ta + ((wave - rel0) % NW + NW) % NW;
     const size_t seq_off = ((size_t)b_cur * a.m_cap * a.G + (size_t)g) * DH * sizeof(T);
     const size_t new_off = ((size_t)b_cur * a.G + (size_t)g) * DH * sizeof(T);
+    // Row of this lane in tile tl: pointers (the appended row comes from
+    // k_new / v_new) and whether it is visible.
+    auto row_ptrs = [&](int tl, const char*& kp, const char*& vp) {
+      const int pos = j0 + tl * kTileRows + row;
+      const bool is_new = (pos == app_pos);
+      kp = is_new ? a.k_new + new_off : a.k + seq_off + (size_t)pos * row_stride;
+      vp = is_new ? a.v_new + new_off : a.v + seq_off + (size_t)pos * row_stride;
+      return pos < L;
+    };
+    // The concat: the lane holding the appended row stores it into the cache.
+    auto store_new_row = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
+      const int pos = j0 + tl * kTileRows + row;
+      if (pos != app_pos) return;
+      char* kc = a.k + seq_off + (size_t)pos * row_stride;
+      char* vc = a.v + seq_off + (size_t)pos * row_stride;
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        *reinterpret_cast<u32x4*>(kc + (2 * c + half) * 16) = kr[c];
+        *reinterpret_cast<u32x4*>(vc + (2 * c + half) * 16) = vr[c];
+      }
+    };
+    WaveState<ND> st;
+    st.reset();
+    auto update = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
+      const int pos0 = j0 + tl * kTileRows;
+      if (pos0 + kTileRows <= L)
+        tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+      else
+        tile_update<T, DH, false>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+    };
 
-    for (int tile = ta + wave; tile < te; tile += NW) {
+    stage_q<T, DH, NW>(a, s_q, b_cur, g, wave, lane);
+    __syncthreads();
+    for (; tile < te; tile += NW) {
       const int pos0 = j0 + tile * kTileRows;
-      const int pos = pos0 + row;
       u32x4 kr[NQ], vr[NQ];
       if (pos0 + kTileRows <= L && app_pos < pos0) {
-        const size_t off = seq_off + (size_t)pos * row_stride;
+        const size_t off = seq_off + (size_t)(pos0 + row) * row_stride;
         load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
         tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
       } else {
         // last tile of the segment: ragged, and/or holding the appended row
-        const bool is_new = (pos == app_pos);
-        const char* kp = is_new ? a.k_new + new_off : a.k + seq_off + (size_t)pos * row_stride;
-        const char* vp = is_new ? a.v_new + new_off : a.v + seq_off + (size_t)pos * row_stride;
-        load_kv<NQ, false>(kp, vp, pos < L, half, kr, vr);
-        if (is_new) {  // the concat: store the new row into the cache
-          char* kc = a.k + seq_off + (size_t)pos * row_stride;
-          char* vc = a.v + seq_off + (size_t)pos * row_stride;
-#pragma unroll
-          for (int c = 0; c < NQ; ++c) {
-            *reinterpret_cast<u32x4*>(kc + (2 * c + half) * 16) = kr[c];
-            *reinterpret_cast<u32x4*>(vc + (2 * c + half) * 16) = vr[c];
-          }
-        }
-        if (pos0 + kTileRows <= L)
-          tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
-        else
-          tile_update<T, DH, false>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+        const char *kp, *vp;
+        const bool valid = row_ptrs(tile, kp, vp);
+        load_kv<NQ, false>(kp, vp, valid, half, kr, vr);
+        store_new_row(tile, kr, vr);
+        update(tile, kr, vr);
       }
     }
 
@@ -414,7 +458,7 @@ struct CombineArgs {
   int32_t* lens;         // bumped when the decode appended
   int32_t* err_flag;     // nullable
   char* o;
-  int b, h, G, hg, m_cap, rec_floats, grid;
+  int b, h, G, hg, m_cap, rec_floats, grid, min_tiles;
   int append;
 };
 
@@ -447,8 +491,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int nb = a.prefix[bi + 1] - a.prefix[bi];
   if (nb == 0) return;
   const int64_t Tt = (int64_t)a.prefix[a.b] * a.G;
+  const int W = effective_grid(Tt, (int64_t)a.prefix[a.b + 1] * a.G, a.grid, a.min_tiles);
   const int64_t S0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * nb;
-  const int wf = wg_of(S0, Tt, a.grid), wl = wg_of(S0 + nb - 1, Tt, a.grid);
+  const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
 
   const int hd0 = blockIdx.y * HPB;
@@ -459,17 +504,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // walk the contributing workgroups kMaxRec at a time
   for (int w0 = wf; w0 <= wl; w0 += kMaxRec) {
     const int w1 = min(wl, w0 + kMaxRec - 1);
+    const int n = w1 - w0 + 1;
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int w = w0; w <= w1; ++w) {
-        if (wg_start(Tt, w, a.grid) == wg_start(Tt, w + 1, a.grid)) { s_rec[n++] = -1; continue; }
-        const int slot = (w == wf && wg_start(Tt, w, a.grid) < S0) ? 1 : 0;
-        s_rec[n++] = w * 2 + slot;
-      }
+    // record index of workgroup w0 + k (-1: empty range, wrote nothing)
+    for (int k = threadIdx.x; k < n; k += 256) {
+      const int w = w0 + k;
+      int r = -1;
+      if (wg_start(Tt, w, W) < wg_start(Tt, w + 1, W))
+        r = w * 2 + ((w == wf && wg_start(Tt, w, W) < S0) ? 1 : 0);
+      s_rec[k] = r;
     }
     __syncthreads();
-    const int n = w1 - w0 + 1;
+    // the first kPre records' accumulators are fetched together with the maxima
+    constexpr int kPre = 8;
+    f32x4 pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      pre[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < n && s_rec[u] >= 0 && hd < a.hg)
+        pre[u] = *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[u] * a.rec_floats +
+                                                 (size_t)hd * DH + 4 * d4);
+    }
     for (int e = threadIdx.x; e < n * HPB; e += 256) {
       const int k = e / HPB, h2 = e % HPB;
       float m = kNegInf;
@@ -497,7 +552,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __syncthreads();
     if (hd < a.hg) {
       acc *= s_inv[hl];
-      int k = 0;
+#pragma unroll
+      for (int u = 0; u < kPre; ++u)
+        if (u < n) acc += pre[u] * s_f[u][hl];
+      int k = kPre;
       for (; k + 4 <= n; k += 4) {
         f32x4 x[4];
 #pragma unroll
@@ -534,9 +592,10 @@ size_t decode_record_bytes(int hg, int dh) {
   return f * sizeof(float);
 }
 
-// Schedule header: the [b + 1] tile prefix, padded to 256 bytes.
+// Schedule header: the [b + 1] tile prefix and the count of non-empty
+// sequences, padded to 256 bytes.
 size_t decode_records_offset(int b) {
-  return (((size_t)b + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return (((size_t)b + 2) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
 int decode_grid_cap(int b, int G, int m_cap) {
@@ -616,6 +675,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   ca.m_cap = p.m_cap;
   ca.rec_floats = a.rec_floats;
   ca.grid = grid;
+  ca.min_tiles = kDecodeWaves;
   ca.append = p.k_new != nullptr;
   constexpr int kHeadsPerBlock = 256 / (DH / 4);
   dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));
