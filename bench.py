@@ -36,12 +36,65 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_c3_hbm_traffic.md")
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
 METRIC = "MQA decode steps/s + effective KV GB/s (%HBM peak), b=64 h=32 d=128 m=8K"
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events for kernel timing, created without the system-scope
+    fence that a default event record adds, so that an event pair around one
+    kernel measures that kernel (as the profiler's dispatch timestamps do)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            for e in (e0, e1):
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE):
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+            self.pairs.append((e0.value, e1.value))
+
+    def elapsed_s(self, i):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.pairs[i][0], self.pairs[i][1]):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e-3
+
+    def close(self):
+        for e0, e1 in self.pairs:
+            self.hip.hipEventDestroy(e0)
+            self.hip.hipEventDestroy(e1)
+
+
+def measured_traffic():
+    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings),
+    or None when the kernel sources changed since those counters were taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.strip().startswith("traffic-json:"))
+    except (OSError, StopIteration):
+        return None
+    info = json.loads(line.split("traffic-json:", 1)[1])
+    h = hashlib.sha256()
+    for f in info["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return info["traffic_bytes_per_launch"] if h.hexdigest() == info["sources_sha256"] else None
 
 
 # --------------------------------------------------------------------------- decode
@@ -152,12 +205,7 @@ class DecodeBench:
         stream right around it) and its algorithmic bytes per launch, over n eager
         steps queued behind a GPU sleep so that launches never wait for the host."""
         torch = self.torch
-        evs = []
-        for _ in range(n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            e1.record()
-            evs.append((e0, e1))
+        ev = HipEvents(n)
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * 0.02))      # ~20 ms of GPU spin: launches queue up
         kv = 0
@@ -166,9 +214,10 @@ class DecodeBench:
             r = i % self.R
             self.appends[r] += 1 if self.cfg.append else 0
             kv += self.kv_bytes(r)
-            self.steps[r](evs[i])
+            self.steps[r](ev.pairs[i])
         torch.cuda.synchronize()
-        dur = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+        dur = [ev.elapsed_s(i) for i in range(n)]
+        ev.close()
         return sum(dur) / n, (kv + n * other) / n, kv / n
 
 
@@ -266,6 +315,8 @@ def main():
     ap.add_argument("--kernel-steps", type=int, default=64)
     ap.add_argument("--two-call", action="store_true",
                     help="append with mqa_kv_append, then mqa_decode (two launches per step)")
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
+                    help="also run 3 plain device copies of MB MiB (calibrates profiler byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -282,6 +333,16 @@ def main():
     torch.cuda.set_device(0)
     use_graph = not args.eager
 
+    if args.probe_copy:
+        n = args.probe_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"probe copy: 3 x {args.probe_copy} MiB read + written")
+        del src, dst
+
     log("headline: serving decode c3 (b=64, h=32, G=1, d_h=128, lens U[1,8192] + append)")
     head = DecodeBench(W.C3, args.rotate, torch, mqa, fused=not args.two_call)
     res = decode_result(head, args.steps, args.warmup, use_graph)
@@ -291,7 +352,7 @@ def main():
     achieved = kbytes / kdur / 1e9
     log(f"decode kernel avg {kdur * 1e6:.2f} us, {achieved:.1f} GB/s")
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=measured_traffic(),
                     kernel="decode_kernel<bf16,128,8>",
                     avg_launch_us=round(kdur * 1e6, 3),
                     algorithmic_bytes_per_launch=int(kbytes))
@@ -337,11 +398,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "serving MQA decode: kv append + decode (split-K, in-kernel combine)",
+        "config": {"workload": "serving MQA decode: kv append + split-K decode + combine",
                    "b": 64, "h": 32, "G": 1, "d_h": 128, "lens": "uniform [1,8192] + 1 append",
                    "m_cap": W.C3.m_cap, "rotated_caches": args.rotate,
                    "launch": ("eager" if args.eager else "hip-graph") +
-                             (", two calls" if args.two_call else ", one fused kernel")},
+                             (", kv_append + decode + combine kernels" if args.two_call
+                              else ", decode (append fused) + combine kernels")},
         "kv_gbps": round(res["kv_gbps"], 1),
         "kv_frac_of_hbm_peak": round(res["kv_frac_of_peak"], 4),
         "roofline": roofline,

@@ -152,6 +152,15 @@ def _shape_only(K):
     return _Cache(None, None, b, m_cap, G, dh, _DTYPES.get(K.dtype, -1))
 
 
+def _event_handle(e):
+    """hipEvent_t of a torch.cuda.Event (already created) or a raw handle."""
+    h = e.cuda_event if isinstance(e, torch.cuda.Event) else e
+    h = h.value if isinstance(h, ctypes.c_void_p) else h
+    if not h:
+        raise ValueError("timing events must be created (recorded once) before use")
+    return ctypes.c_void_p(h)
+
+
 def _check_new_rows(k_new, v_new, K, lens):
     b, _, G, dh = K.shape
     if k_new.shape != (b, G, dh) or v_new.shape != (b, G, dh):
@@ -207,9 +216,7 @@ def _decode_call(q, k_new, v_new, K, V, lens, scale, window, out, workspace, err
     c = _cache(K, V)
     ev0 = ev1 = None
     if events is not None:
-        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in events)
-        if not ev0.value or not ev1.value:
-            raise ValueError("timing events must be created (recorded once) before use")
+        ev0, ev1 = (_event_handle(e) for e in events)
     _check("mqa_decode_ex", _lib.mqa_decode_ex(
         _ptr(q), _ptr(k_new), _ptr(v_new), q.shape[1], ctypes.byref(c), _ptr(lens),
         _ptr(err_flag), float(scale), int(window), _ptr(out), _ptr(workspace),
@@ -320,8 +327,7 @@ class DecodeStep:
         if events is None:
             rc = self._fx(*self._decode, s, None, None)
         else:
-            rc = self._fx(*self._decode, s, ctypes.c_void_p(events[0].cuda_event),
-                          ctypes.c_void_p(events[1].cuda_event))
+            rc = self._fx(*self._decode, s, _event_handle(events[0]), _event_handle(events[1]))
         if rc:
             raise MQAError("mqa_decode_ex", rc)
         return self.out
