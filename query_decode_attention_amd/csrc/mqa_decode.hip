@@ -464,17 +464,22 @@ struct CombineArgs {
 
 // Merge of the partial records of one (sequence, group) segment:
 // M = max_k m_k, weights f_k = exp2(m_k - M), o = sum_k f_k acc_k / sum_k f_k l_k
-// (the softmax re-associated exactly).  The per-record weights go through LDS
-// so that the loads of the final sum are independent of each other.
+// (the softmax re-associated exactly).  Thread (head, d4) fetches a whole
+// batch of records at once -- its float4 of every accumulator plus the head's
+// max and sum, which the 32 threads of a head read at one address -- so a
+// batch costs one memory round trip; there is no LDS and no barrier.
 // Block (seg, y) handles the heads [y*HPB, (y+1)*HPB) of segment seg.
+//
+// Every workgroup of the decode grid has a non-empty tile range (the
+// effective grid never exceeds the tile count T, since each non-empty segment
+// holds at least one tile), so every workgroup in [wf, wl] wrote a record for
+// this segment: slot 1 for wf when its range began in an earlier segment,
+// slot 0 otherwise.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int kD4 = DH / 4;            // float4 words per head row
   constexpr int HPB = 256 / kD4;         // heads per block
-  constexpr int kMaxRec = 128;           // records held in LDS per pass
-  __shared__ float s_f[kMaxRec][HPB];
-  __shared__ float s_inv[HPB];
-  __shared__ int s_rec[kMaxRec];
+  constexpr int kBatch = 16;             // records per round trip
 
   if (a.append && blockIdx.x == 0 && blockIdx.y == 0) {
     int over = 0;
@@ -495,93 +500,51 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t S0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * nb;
   const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
+  const int first_slot = (wg_start(Tt, wf, W) < S0) ? 1 : 0;
 
-  const int hd0 = blockIdx.y * HPB;
   const int hl = threadIdx.x / kD4, d4 = threadIdx.x % kD4;
-  const int hd = hd0 + hl;
+  const int hd = blockIdx.y * HPB + hl;
+  if (hd >= a.hg) return;
+  const float* acc_at = a.records + (size_t)hd * DH + 4 * d4;
+  const float* m_at = a.records + (size_t)a.hg * DH + hd;
+  const float* l_at = m_at + a.hg;
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float M = kNegInf, lsum = 0.f;        // running (per head, kept by thread d4 == 0)
-  // walk the contributing workgroups kMaxRec at a time
-  for (int w0 = wf; w0 <= wl; w0 += kMaxRec) {
-    const int w1 = min(wl, w0 + kMaxRec - 1);
-    const int n = w1 - w0 + 1;
-    __syncthreads();
-    // record index of workgroup w0 + k (-1: empty range, wrote nothing)
-    for (int k = threadIdx.x; k < n; k += 256) {
-      const int w = w0 + k;
-      int r = -1;
-      if (wg_start(Tt, w, W) < wg_start(Tt, w + 1, W))
-        r = w * 2 + ((w == wf && wg_start(Tt, w, W) < S0) ? 1 : 0);
-      s_rec[k] = r;
-    }
-    __syncthreads();
-    // the first kPre records' accumulators are fetched together with the maxima
-    constexpr int kPre = 8;
-    f32x4 pre[kPre];
+  float M = kNegInf, lsum = 0.f;
+  for (int w0 = wf; w0 <= wl; w0 += kBatch) {
+    f32x4 x[kBatch];
+    float m[kBatch], l[kBatch];
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      pre[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < n && s_rec[u] >= 0 && hd < a.hg)
-        pre[u] = *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[u] * a.rec_floats +
-                                                 (size_t)hd * DH + 4 * d4);
-    }
-    for (int e = threadIdx.x; e < n * HPB; e += 256) {
-      const int k = e / HPB, h2 = e % HPB;
-      float m = kNegInf;
-      if (s_rec[k] >= 0 && hd0 + h2 < a.hg)
-        m = a.records[(size_t)s_rec[k] * a.rec_floats + (size_t)a.hg * DH + hd0 + h2];
-      s_f[k][h2] = m;
-    }
-    __syncthreads();
-    if (threadIdx.x < HPB && hd0 + threadIdx.x < a.hg) {
-      const int h2 = threadIdx.x;
-      float Mn = M;
-      for (int k = 0; k < n; ++k) Mn = fmaxf(Mn, s_f[k][h2]);
-      const float Ms = (Mn == kNegInf) ? 0.f : Mn;
-      float l = lsum * fast_exp2(M - Ms);
-      for (int k = 0; k < n; ++k) {
-        const float f = fast_exp2(s_f[k][h2] - Ms);
-        s_f[k][h2] = f;
-        if (s_rec[k] >= 0)
-          l += f * a.records[(size_t)s_rec[k] * a.rec_floats + (size_t)a.hg * DH + a.hg + hd0 + h2];
+    for (int u = 0; u < kBatch; ++u) {
+      const int w = w0 + u;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[u] = kNegInf;
+      l[u] = 0.f;
+      if (w <= wl) {
+        const size_t r = (size_t)(2 * w + (w == wf ? first_slot : 0)) * a.rec_floats;
+        x[u] = *reinterpret_cast<const f32x4*>(acc_at + r);
+        m[u] = m_at[r];
+        l[u] = l_at[r];
       }
-      s_inv[h2] = fast_exp2(M - Ms);  // rescale of the running sum of earlier passes
-      M = Mn;
-      lsum = l;
     }
-    __syncthreads();
-    if (hd < a.hg) {
-      acc *= s_inv[hl];
+    float Mn = M;
 #pragma unroll
-      for (int u = 0; u < kPre; ++u)
-        if (u < n) acc += pre[u] * s_f[u][hl];
-      int k = kPre;
-      for (; k + 4 <= n; k += 4) {
-        f32x4 x[4];
+    for (int u = 0; u < kBatch; ++u) Mn = fmaxf(Mn, m[u]);
+    const float Ms = (Mn == kNegInf) ? 0.f : Mn;
+    const float sc = fast_exp2(M - Ms);
+    acc *= sc;
+    lsum *= sc;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (s_rec[k + u] >= 0)
-            x[u] = *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[k + u] * a.rec_floats +
-                                                   (size_t)hd * DH + 4 * d4);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc += x[u] * s_f[k + u][hl];
-      }
-      for (; k < n; ++k)
-        if (s_rec[k] >= 0)
-          acc += *reinterpret_cast<const f32x4*>(a.records + (size_t)s_rec[k] * a.rec_floats +
-                                                 (size_t)hd * DH + 4 * d4) * s_f[k][hl];
+    for (int u = 0; u < kBatch; ++u) {
+      const float f = fast_exp2(m[u] - Ms);
+      acc += x[u] * f;
+      lsum += l[u] * f;
     }
+    M = Mn;
   }
-  __syncthreads();
-  if (threadIdx.x < HPB) s_inv[threadIdx.x] = 1.0f / lsum;
-  __syncthreads();
-  if (hd < a.hg) {
-    const float inv = s_inv[hl];
-    T* op = reinterpret_cast<T*>(a.o) + ((size_t)bi * a.h + (size_t)g * a.hg + hd) * DH + 4 * d4;
-    store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  }
+  const float inv = 1.0f / lsum;
+  T* op = reinterpret_cast<T*>(a.o) + ((size_t)bi * a.h + (size_t)g * a.hg + hd) * DH + 4 * d4;
+  store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
 // ------------------------------------------------------------------- host ----
