@@ -14,8 +14,14 @@
 // are cut into tiles of 32.  All tiles of all segments form one flat list of
 // T tiles; workgroup w of a grid of W takes tiles [T*w/W, T*(w+1)/W), so every
 // workgroup streams the same number of bytes whatever the length mix.  Each
-// wave derives this schedule from lens by itself (wave-wide scan), so no host
-// synchronisation and no workgroup barrier precede the first K/V loads.
+// wave derives this schedule from lens by itself (wave-wide scan) and keeps
+// the lens entries it needs in registers, so the schedule costs no host
+// synchronisation, no barrier and one read of lens.
+//
+// Q.  A segment's Q^T operand is staged in LDS once for all its tiles.  When
+// a workgroup's range goes on past the current segment, the next segment's
+// Q^T is copied into a second LDS buffer while the current one streams, so
+// the switch to it costs no memory round trip.
 //
 // Inside a workgroup, wave k takes every NW-th tile of a segment.  At the end
 // of a segment all waves park their (max, sum, accumulator) in LDS and the
@@ -98,8 +104,8 @@ struct SeqView {
   int j0, L, app_pos;
 };
 
-__device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
-  const int raw = a.lens[bi];
+// From the raw lens entry of the sequence.
+__device__ __forceinline__ SeqView seq_view_raw(const DecodeArgs& a, int raw) {
   int l = raw < 0 ? 0 : (raw > a.m_cap ? a.m_cap : raw);
   int app = -1;
   if (a.k_new && raw >= 0 && raw < a.m_cap) {
@@ -111,6 +117,10 @@ __device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
   s.j0 = (a.window > 0 && l > a.window) ? l - a.window : 0;
   s.app_pos = app;
   return s;
+}
+
+__device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
+  return seq_view_raw(a, a.lens[bi]);
 }
 
 __device__ __forceinline__ int tiles_of(const SeqView& s) {
@@ -230,20 +240,46 @@ struct SlotIndex {
   __device__ __forceinline__ int d() const { return 32 * blk + 8 * r4 + 4 * (lane >> 5); }
 };
 
-// Q^T operand of group g of sequence bi, staged once in LDS in lane order:
-// chunk c of lane l is head l % 32, 16-byte chunk 2c + l / 32 of its row
-// (zeros for heads >= h/G).
+// 16 bytes per lane from `src` straight into LDS word `lane` of `dst` (the
+// direct-to-LDS load path; the LDS base must be the same for the whole wave).
+// Completion is counted by vmcnt.
+__device__ __forceinline__ void load_to_lds(const char* src, u32x4* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
+                                   16, 0, 0);
+}
+
+// Q^T operand of group g of sequence bi in LDS, lane order: chunk c of lane l
+// is head l % 32, 16-byte chunk 2c + l / 32 of its row.  Columns of heads
+// >= h/G repeat a real head, so they hold finite values; every head column
+// has its own softmax and those columns are never written out.
+__device__ __forceinline__ const char* q_row(const DecodeArgs& a, int bi, int g, int lane,
+                                             int row_bytes) {
+  const int row = lane & 31;
+  const int qrow = row < a.hg ? row : row % a.hg;
+  return a.q + ((size_t)bi * a.h + (size_t)g * a.hg + qrow) * row_bytes;
+}
+
+// Every wave stages its share of the chunks through registers; the caller
+// barriers before the operand is read.
 template <typename T, int DH, int NW>
 __device__ __forceinline__ void stage_q(const DecodeArgs& a, u32x4 (*s_q)[64], int bi, int g,
                                         int wave, int lane) {
   constexpr int NQ = TileShape<T, DH>::NQ;
-  const int row = lane & 31, half = lane >> 5;
-  const char* qp = a.q + ((size_t)bi * a.h + (size_t)g * a.hg + row) * DH * sizeof(T);
-  for (int c = wave; c < NQ; c += NW) {
-    u32x4 x = u32x4{0u, 0u, 0u, 0u};
-    if (row < a.hg) x = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
-    s_q[c][lane] = x;
-  }
+  const int half = lane >> 5;
+  const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
+  for (int c = wave; c < NQ; c += NW) s_q[c][lane] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+}
+
+// The same chunks as stage_q, copied straight into LDS (no registers, so the
+// copy can be in flight while the wave streams tiles); complete once this
+// wave's vmcnt reaches 0.
+template <typename T, int DH, int NW>
+__device__ __forceinline__ void copy_q(const DecodeArgs& a, u32x4 (*s_q)[64], int bi, int g,
+                                       int wave, int lane) {
+  constexpr int NQ = TileShape<T, DH>::NQ;
+  const int half = lane >> 5;
+  const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
+  for (int c = wave; c < NQ; c += NW) load_to_lds(qp + (2 * c + half) * 16, &s_q[c][0]);
 }
 
 // ------------------------------------------------------------ decode: kernel ----
@@ -253,18 +289,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
   constexpr int kWords = ND * 4 * 64;  // f32x4 words per slot
+  // Two Q^T buffers when they fit: the next segment's Q is fetched while the
+  // current one streams.
+  constexpr int kQBufs =
+      NW * sizeof(WaveSlot<ND>) + 2 * NQ * 64 * sizeof(u32x4) + 256 <= 160 * 1024 ? 2 : 1;
   __shared__ WaveSlot<ND> s_slot[NW];
-  __shared__ u32x4 s_q[NQ][64];        // Q^T operand of the current segment
-  __shared__ float s_fold[2][32];      // per-head max and sum of the folded state
+  __shared__ u32x4 s_q[kQBufs][NQ][64];  // Q^T operand(s)
+  __shared__ float s_fold[2][32];        // per-head max and sum of the folded state
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 31, half = lane >> 5;
 
   // ---- schedule (each wave on its own) ----
-  int total = 0, nonempty = 0;
+  // raw0: lens entry of sequence `lane` (the first 64), reused below.
+  int total = 0, nonempty = 0, raw0 = 0;
   for (int c = 0; c < a.b; c += 64) {
-    int v = 0;
-    if (c + lane < a.b) v = tiles_of(seq_view(a, c + lane));
+    int raw = 0, v = 0;
+    if (c + lane < a.b) {
+      raw = a.lens[c + lane];
+      v = tiles_of(seq_view_raw(a, raw));
+    }
+    if (c == 0) raw0 = raw;
     const int incl = wave_incl_scan(v, lane);
     if (blockIdx.x == 0 && wave == 0 && c + lane < a.b) a.prefix[c + lane] = total + incl - v;
     total += __shfl(incl, 63, 64);
@@ -281,13 +326,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int W = effective_grid(Tt, (int64_t)nonempty * a.G, gridDim.x, NW);
   const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
 
+  // lens entries of sequences cbase .. cbase + 63, one per lane: the segment
+  // walk below reads lens from here, not from memory.
+  int cbase = 0, craw = raw0;
   int b_cur = a.b;
   int64_t seg_base = 0;
   if (t0 < t1) {
     int run = 0;
     for (int c = 0; c < a.b; c += 64) {
-      int v = 0;
-      if (c + lane < a.b) v = tiles_of(seq_view(a, c + lane));
+      int raw = raw0, v = 0;
+      if (c > 0) raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
+      if (c + lane < a.b) v = tiles_of(seq_view_raw(a, raw));
       const int incl = wave_incl_scan(v, lane);
       const int64_t lo = (int64_t)(run + incl - v) * a.G, hi = (int64_t)(run + incl) * a.G;
       const uint64_t hit = __ballot(c + lane < a.b && v > 0 && lo <= t0 && t0 < hi);
@@ -295,6 +344,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const int src = __builtin_ctzll(hit);
         b_cur = c + src;
         seg_base = (int64_t)(run + __shfl(incl - v, src, 64)) * a.G;
+        cbase = c;
+        craw = raw;
         break;
       }
       run += __shfl(incl, 63, 64);
@@ -320,10 +371,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   sel.init(row, half);
   const size_t row_stride = (size_t)a.G * DH * sizeof(T);
   int64_t t = t0;
+  // lens entry of sequence bi (uniform), refilling the lane cache by chunks
+  auto raw_of = [&](int bi) {
+    if (bi < cbase || bi >= cbase + 64) {
+      cbase = bi;
+      craw = (bi + lane < a.b) ? a.lens[bi + lane] : 0;
+    }
+    return __shfl(craw, bi - cbase, 64);
+  };
+  // The segment after (bi, gi) in flat order, skipping empty sequences
+  // (bn == b: none).  Uniform.
+  auto next_seg = [&](int bi, int gi, int& bn, int& gn) {
+    bn = bi;
+    gn = gi + 1;
+    if (gn == a.G) {
+      gn = 0;
+      do {
+        ++bn;
+      } while (bn < a.b && tiles_of(seq_view_raw(a, raw_of(bn))) == 0);
+    }
+  };
+  int qb = 0;             // Q^T buffer of the current segment
+  bool q_staged = false;  // ... already copied during the previous segment
   bool first = true;
 
   while (t < t1 && b_cur < a.b) {
-    const SeqView sv = seq_view(a, b_cur);
+    const SeqView sv = seq_view_raw(a, raw_of(b_cur));
     const int j0 = __builtin_amdgcn_readfirstlane(sv.j0);
     const int L = __builtin_amdgcn_readfirstlane(sv.L);
     const int app_pos = __builtin_amdgcn_readfirstlane(sv.app_pos);
@@ -337,7 +410,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int ta = (int)(t - seg0);
     const int te = (int)((t1 < seg0 + nb ? t1 : seg0 + nb) - seg0);
     const bool complete = (ta == 0 && te == nb);
-    const int seg = b_cur * a.G + g;
+    const bool last_seg = (seg0 + te >= t1);
 
     // ---- this wave's tiles ----
     // Tiles go round-robin over the waves by their index in the workgroup's
@@ -373,20 +446,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     auto update = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
       const int pos0 = j0 + tl * kTileRows;
       if (pos0 + kTileRows <= L)
-        tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, true>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
       else
-        tile_update<T, DH, false>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, false>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
     };
 
-    stage_q<T, DH, NW>(a, s_q, b_cur, g, wave, lane);
+    // ---- Q^T of this segment, and the copy of the next one's ----
+    if (!q_staged) stage_q<T, DH, NW>(a, s_q[qb], b_cur, g, wave, lane);
     __syncthreads();
+    // When the range goes on, the next segment's Q^T is copied into the
+    // other buffer now and lands while this segment streams.
+    bool next_staged = false;
+    if constexpr (kQBufs == 2) {
+      if (!last_seg) {
+        int bn, gn;
+        next_seg(b_cur, g, bn, gn);
+        copy_q<T, DH, NW>(a, s_q[qb ^ 1], bn, gn, wave, lane);
+        next_staged = true;
+      }
+    }
+
     for (; tile < te; tile += NW) {
       const int pos0 = j0 + tile * kTileRows;
       u32x4 kr[NQ], vr[NQ];
       if (pos0 + kTileRows <= L && app_pos < pos0) {
         const size_t off = seq_off + (size_t)(pos0 + row) * row_stride;
         load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
-        tile_update<T, DH, true>(st, kr, vr, s_q, lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, true>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
       } else {
         // last tile of the segment: ragged, and/or holding the appended row
         const char *kp, *vp;
@@ -396,6 +482,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         update(tile, kr, vr);
       }
     }
+    // This wave's part of the next Q^T has landed before the barriers below,
+    // which publish it.
+    if (next_staged) __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // ---- fold the waves: park in LDS, combine in a fixed order ----
     park<ND>(st, s_slot[wave], lane);
@@ -437,9 +526,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-
     __syncthreads();  // LDS slots are reused by the next segment
 
+    if (next_staged) qb ^= 1;
+    q_staged = next_staged;
     first = false;
     t = seg0 + te;
     if (g == a.G - 1 && te == nb) {
@@ -447,7 +537,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       ++b_cur;
     }
   }
-
 }
 
 // --------------------------------------------------------- combine kernel ----
