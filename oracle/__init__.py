@@ -51,6 +51,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.oracle_kv_append.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+        lib.oracle_kv_reorder.argtypes = [I, I, I, I, I, I, P, P, P, P, P]
         lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, D, I, P, I]
         lib.oracle_decode_weights.argtypes = [I, I, I, I, I, I, P, P, P, P, D, I, I, I, P]
         lib.oracle_prefill.argtypes = [I, I, I, I, I, I, P, P, P, D, P, ctypes.c_int64, P, I]
@@ -112,6 +113,29 @@ def kv_append(k_new, v_new, K, V, lens):
     if rc != 0:
         raise ValueError("oracle_kv_append rejected its arguments")
     return over.value
+
+
+def kv_reorder(K, V, lens, parent, beam):
+    """In-place beam reorder on numpy arrays (raw storage).  Returns the number
+    of invalid parents.
+
+    K, V: [b, m_cap, G, dh] (float32 or uint16 bf16 bits); lens, parent:
+    int32 [b]; hypothesis i takes the cache of (i // beam) * beam + parent[i].
+    """
+    assert isinstance(K, np.ndarray) and K.flags.c_contiguous and isinstance(V, np.ndarray)
+    assert V.flags.c_contiguous and V.shape == K.shape and V.dtype == K.dtype
+    dt = F32 if K.dtype == np.float32 else BF16
+    assert K.dtype in (np.float32, np.uint16)
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    b, m_cap, G, dh = K.shape
+    assert lens.shape == (b,) and par.shape == (b,)
+    bad = ctypes.c_int32(0)
+    rc = _load().oracle_kv_reorder(dt, b, G, dh, m_cap, int(beam), _ptr(par), _ptr(K), _ptr(V),
+                                   _ptr(lens), ctypes.byref(bad))
+    if rc != 0:
+        raise ValueError("oracle_kv_reorder rejected its arguments")
+    return bad.value
 
 
 def decode(q, K, V, lens, scale, window=0, nthreads=None) -> np.ndarray:

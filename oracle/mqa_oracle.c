@@ -59,6 +59,47 @@ int oracle_kv_append(int dtype, int b, int G, int dh, int m_cap,
   return ORACLE_OK;
 }
 
+/* ----------------------------------------------------------------- reorder */
+
+int oracle_kv_reorder(int dtype, int b, int G, int dh, int m_cap, int beam,
+                      const int32_t* parent, void* K, void* V, int32_t* lens,
+                      int32_t* bad) {
+  if (check_common(dtype, b, G, G, dh) != ORACLE_OK || m_cap <= 0 || beam <= 0 || b % beam != 0)
+    return ORACLE_EINVAL;
+  const size_t row = (size_t)G * dh * elem_size(dtype);      /* one position, all groups */
+  const size_t seq = row * (size_t)m_cap;                     /* one hypothesis */
+  /* the cache as it was: every copy reads from here */
+  char* K0 = (char*)malloc(seq * (size_t)b);
+  char* V0 = (char*)malloc(seq * (size_t)b);
+  int32_t* lens0 = (int32_t*)malloc(sizeof(int32_t) * (size_t)(b > 0 ? b : 1));
+  if (!K0 || !V0 || !lens0) {
+    free(K0);
+    free(V0);
+    free(lens0);
+    return ORACLE_EINVAL;
+  }
+  memcpy(K0, K, seq * (size_t)b);
+  memcpy(V0, V, seq * (size_t)b);
+  memcpy(lens0, lens, sizeof(int32_t) * (size_t)b);
+  int32_t nbad = 0;
+  for (int i = 0; i < b; ++i) {
+    const int32_t p = parent[i];
+    if (p < 0 || p >= beam) { ++nbad; continue; }
+    const int src = (i / beam) * beam + p;
+    int32_t L = lens0[src];
+    if (L < 0) L = 0;
+    if (L > m_cap) L = m_cap;
+    memcpy((char*)K + (size_t)i * seq, K0 + (size_t)src * seq, (size_t)L * row);
+    memcpy((char*)V + (size_t)i * seq, V0 + (size_t)src * seq, (size_t)L * row);
+    lens[i] = lens0[src];
+  }
+  free(K0);
+  free(V0);
+  free(lens0);
+  if (bad) *bad = nbad;
+  return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------ decode */
 
 typedef struct {

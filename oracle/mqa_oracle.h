@@ -44,6 +44,22 @@ int oracle_kv_append(int dtype, int b, int G, int dh, int m_cap,
                      const void* k_new, const void* v_new, void* K, void* V,
                      int32_t* lens, int32_t* overflow);
 
+/* Beam reorder of the cache.  Beam search over the incremental decoder (the
+ * study notes' section 6.2 beam-4 measurements) keeps `beam` hypotheses per
+ * source; before a step every hypothesis continues one hypothesis of its own
+ * source and inherits its cache.  The pages do not spell the mechanics out;
+ * the reading taken: the b cache rows form b / beam groups of `beam`
+ * consecutive hypotheses and, with src(i) = (i / beam) * beam + parent[i],
+ *   K'[i, j] = K[src(i), j] and V'[i, j] = V[src(i), j] for j < L(src(i)),
+ *   lens'[i] = lens[src(i)],
+ * all read from the cache as it was before the call (L = lens clamped to
+ * [0, m_cap]).  Positions j >= L(src(i)) of row i keep their contents.  A
+ * parent outside [0, beam) leaves row i and lens[i] as they were and is
+ * counted in *bad. */
+int oracle_kv_reorder(int dtype, int b, int G, int dh, int m_cap, int beam,
+                      const int32_t* parent, void* K, void* V, int32_t* lens,
+                      int32_t* bad);
+
 /* One decode step over the cache.  L_b = clamp(lens[b], 0, m_cap).  window > 0
  * restricts the visible positions to the last `window` ones (local attention,
  * study notes section 6.4); window <= 0 means all of them.  An empty row

@@ -302,6 +302,87 @@ def test_append_is_a_bytewise_concat(dtype):
     assert Kr.tobytes() == expK.tobytes() and Vr.tobytes() == expV.tobytes()
 
 
+# ---------------------------------------------------------------- beam reorder
+
+
+def _beam_cache(dtype, seed, b=8, m=7, G=2, dh=64):
+    K, _ = oracle._raw(rand((b, m, G, dh), seed, dtype))
+    V, _ = oracle._raw(rand((b, m, G, dh), seed + 1, dtype))
+    lens = np.random.default_rng(seed).integers(0, m + 1, size=b).astype(np.int32)
+    return K.copy(), V.copy(), lens
+
+
+def test_beam_reorder_identity_changes_nothing():
+    K, V, lens = _beam_cache(torch.bfloat16, 150)
+    K0, V0, l0 = K.copy(), V.copy(), lens.copy()
+    for beam in (1, 2, 4, 8):
+        assert oracle.kv_reorder(K, V, lens, np.arange(8) % beam, beam) == 0
+        assert K.tobytes() == K0.tobytes() and V.tobytes() == V0.tobytes()
+        assert np.array_equal(lens, l0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_beam_reorder_then_decode_equals_decode_of_gathered_rows(dtype):
+    """Route 1: reorder in place, then decode.  Route 2: gather whole parent
+    rows with numpy indexing and decode those.  Decode reads only j < L, so
+    the two agree exactly iff the reorder moved every valid row and length."""
+    b, beam, h, G, dh, m = 8, 4, 4, 2, 64, 7
+    K, V, lens = _beam_cache(dtype, 152, b, m, G, dh)
+    lens[lens == 0] = 1
+    parent = np.array([3, 3, 0, 1, 2, 2, 2, 0], np.int32)   # duplicates, dropped beams
+    src = (np.arange(b) // beam) * beam + parent
+    q = rand((b, h, dh), 153, dtype)
+    want = oracle.decode(q, K[src].copy(), V[src].copy(), lens[src].copy(), 0.125)
+    assert oracle.kv_reorder(K, V, lens, parent, beam) == 0
+    got = oracle.decode(q, K, V, lens, 0.125)
+    assert np.array_equal(got, want)
+
+
+def test_beam_reorder_leaves_positions_past_the_parent_length():
+    K, V, lens = _beam_cache(torch.bfloat16, 154)
+    K0, V0, l0 = K.copy(), V.copy(), lens.copy()
+    parent = np.array([1, 0, 3, 3, 0, 0, 2, 1], np.int32)
+    oracle.kv_reorder(K, V, lens, parent, 4)
+    src = (np.arange(8) // 4) * 4 + parent
+    for i in range(8):
+        L = l0[src[i]]
+        assert lens[i] == L
+        assert K[i, L:].tobytes() == K0[i, L:].tobytes()
+        assert V[i, L:].tobytes() == V0[i, L:].tobytes()
+        assert K[i, :L].tobytes() == K0[src[i], :L].tobytes()
+
+
+def test_beam_reorder_composes():
+    """Reordering by p and then by r equals one reorder by p[r] (within the
+    group), on every valid row and on lens."""
+    b, beam = 8, 4
+    K1, V1, l1 = _beam_cache(torch.float32, 156, b)
+    K2, V2, l2 = K1.copy(), V1.copy(), l1.copy()
+    g = np.random.default_rng(157)
+    p = g.integers(0, beam, size=b).astype(np.int32)
+    r = g.integers(0, beam, size=b).astype(np.int32)
+    base = (np.arange(b) // beam) * beam
+    oracle.kv_reorder(K1, V1, l1, p, beam)
+    oracle.kv_reorder(K1, V1, l1, r, beam)
+    oracle.kv_reorder(K2, V2, l2, p[base + r], beam)
+    assert np.array_equal(l1, l2)
+    for i in range(b):
+        L = max(0, min(int(l1[i]), K1.shape[1]))
+        assert K1[i, :L].tobytes() == K2[i, :L].tobytes()
+        assert V1[i, :L].tobytes() == V2[i, :L].tobytes()
+
+
+def test_beam_reorder_rejects_and_counts_bad_parents():
+    K, V, lens = _beam_cache(torch.bfloat16, 158)
+    K0, l0 = K.copy(), lens.copy()
+    parent = np.array([0, 1, 4, -1, 0, 1, 2, 3], np.int32)   # rows 2, 3 invalid
+    assert oracle.kv_reorder(K, V, lens, parent, 4) == 2
+    assert K[2].tobytes() == K0[2].tobytes() and K[3].tobytes() == K0[3].tobytes()
+    assert lens[2] == l0[2] and lens[3] == l0[3]
+    with pytest.raises(ValueError):
+        oracle.kv_reorder(K, V, lens, np.zeros(8, np.int32), 3)   # 3 does not divide 8
+
+
 def test_append_then_attend_sees_new_token():
     """The concat precedes the logits (paper review section 3), so the new
     token attends to itself: with an empty cache the output is v_new."""
