@@ -79,6 +79,27 @@ typedef struct {
 int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache,
                   int32_t* lens, int32_t* err_flag, void* stream);
 
+/* mqa_kv_reorder -- the cache reorder of beam decoding (the study notes'
+ * section 6.2 reports beam-4 decoding; the pages do not spell out its
+ * mechanics, and this is the plainest reading): the cache->b rows form
+ * cache->b / beam groups of `beam` consecutive hypotheses, and before a step
+ * every hypothesis i continues hypothesis src(i) = (i / beam) * beam +
+ * parent[i] of its own group:
+ *     K[i, j] = K[src(i), j], V[i, j] = V[src(i), j] for j < L(src(i)),
+ *     lens[i] = lens[src(i)],
+ * all read as they were before the call (L = lens clamped to [0, m_cap]).
+ * Positions at or past L(src(i)) of row i keep their contents; a row whose
+ * parent is itself is not touched.  In place: no second cache.
+ *   lens     : device int32 [b], read and rewritten.
+ *   parent   : device int32 [b], beam-local indices in [0, beam).  A parent
+ *              outside that range leaves row i and lens[i] as they were and
+ *              sets *err_flag (optional device int32) to 1.
+ *   beam     : 1 .. 16, dividing cache->b (else MQA_ERR_SHAPE).
+ * Two launches on `stream` (rows, then lens).  The copy is bit-exact.  A beam
+ * step is mqa_kv_reorder followed by mqa_append_decode. */
+int mqa_kv_reorder(const mqa_cache* cache, int32_t* lens, const int32_t* parent, int32_t beam,
+                   int32_t* err_flag, void* stream);
+
 /* Bytes of device workspace a decode needs for `h` query heads over `cache`:
  * a small schedule header (b + 1 ints) followed by the split-K partial
  * results.  Depends only on the shapes, never on the device or on lens.

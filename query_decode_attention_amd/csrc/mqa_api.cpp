@@ -75,7 +75,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MQA_OK : MQA_ERR_LAUN
 
 extern "C" {
 
-int mqa_abi_version(void) { return 200; }
+int mqa_abi_version(void) { return 201; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -110,6 +110,26 @@ int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache, 
   p.m_cap = cache->m_cap;
   p.row_bytes = cache->G * cache->d_h * elem_size(cache->dtype);
   return launch_status(mqa::launch_kv_append(p, static_cast<hipStream_t>(stream)));
+}
+
+int mqa_kv_reorder(const mqa_cache* cache, int32_t* lens, const int32_t* parent, int32_t beam,
+                   int32_t* err_flag, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != MQA_OK) return rc;
+  if (beam < 1 || beam > mqa::kMaxBeam || cache->b % beam != 0) return MQA_ERR_SHAPE;
+  if (cache->b == 0) return MQA_OK;
+  if (!lens || !parent) return MQA_ERR_NULL;
+  mqa::ReorderParams p;
+  p.k = static_cast<char*>(cache->k);
+  p.v = static_cast<char*>(cache->v);
+  p.lens = lens;
+  p.parent = parent;
+  p.err_flag = err_flag;
+  p.b = cache->b;
+  p.m_cap = cache->m_cap;
+  p.beam = beam;
+  p.row_bytes = cache->G * cache->d_h * elem_size(cache->dtype);
+  return launch_status(mqa::launch_kv_reorder(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache) {

@@ -75,6 +75,36 @@ C4 = DecodeConfig("c4_gqa_b32_h64_g8_m32k", torch.bfloat16, b=32, h=64, G=8, dh=
 C5 = PrefillConfig("c5_prefill_b4_n4096", torch.bfloat16, b=4, n=4096, h=32, G=1, dh=128,
                    seed=1005)
 
+@dataclasses.dataclass(frozen=True)
+class BeamConfig:
+    """Beam decoding: ``sources`` source sequences x ``beam`` hypotheses, each
+    hypothesis one cache row; the hypotheses of a source share its length."""
+    name: str
+    dtype: torch.dtype
+    sources: int
+    beam: int
+    h: int
+    G: int
+    dh: int
+    m_cap: int
+    lens_lo: int          # per-source pre-step lens, uniform in [lens_lo, lens_hi]
+    lens_hi: int
+    seed: int
+
+    @property
+    def b(self) -> int:
+        return self.sources * self.beam
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dh)
+
+
+# Beam-4 serving step (the study notes' section 6.2 beam-4 rows) at the c3
+# serving shapes: 16 sources x 4 beams = 64 cache rows.
+BEAM4 = BeamConfig("beam4_b16x4_ragged8k", torch.bfloat16, sources=16, beam=4, h=32, G=1,
+                   dh=128, m_cap=8192 + 256, lens_lo=1, lens_hi=8192, seed=1006)
+
 DECODE_CONFIGS = {c.name: c for c in (C1, C2, C2_MHA, C3, C4)}
 PREFILL_CONFIGS = {C5.name: C5}
 
@@ -115,6 +145,36 @@ def decode_inputs(cfg: DecodeConfig, seed: Optional[int] = None, b: Optional[int
     v_new = _normal(g, (b, cfg.G, cfg.dh), cfg.dtype)
     lens = torch.randint(lo, hi + 1, (b,), generator=g, dtype=torch.int64).to(torch.int32)
     return dict(q=q, K=K, V=V, k_new=k_new, v_new=v_new, lens=lens)
+
+
+def beam_inputs(cfg: BeamConfig, steps: int = 1, seed: Optional[int] = None,
+                sources: Optional[int] = None, m_cap: Optional[int] = None,
+                lens_lo: Optional[int] = None, lens_hi: Optional[int] = None):
+    """CPU tensors for ``steps`` beam steps of ``cfg`` (optionally resized).
+
+    Draw order: K, V [b,m_cap,G,dh]; per-source lens (repeated over the
+    source's beams); then per step: parent int32 [b] uniform in [0, beam),
+    q [b,h,dh], k_new, v_new [b,G,dh].  Stacked per step along dim 0.
+    """
+    src_n = cfg.sources if sources is None else sources
+    b = src_n * cfg.beam
+    m_cap = cfg.m_cap if m_cap is None else m_cap
+    lo = cfg.lens_lo if lens_lo is None else lens_lo
+    hi = cfg.lens_hi if lens_hi is None else lens_hi
+    g = torch.Generator("cpu").manual_seed(cfg.seed if seed is None else seed)
+    K = _normal_chunked(g, (b, m_cap, cfg.G, cfg.dh), cfg.dtype)
+    V = _normal_chunked(g, (b, m_cap, cfg.G, cfg.dh), cfg.dtype)
+    per_src = torch.randint(lo, hi + 1, (src_n,), generator=g, dtype=torch.int64)
+    lens = per_src.repeat_interleave(cfg.beam).to(torch.int32)
+    parent, q, k_new, v_new = [], [], [], []
+    for _ in range(steps):
+        parent.append(torch.randint(0, cfg.beam, (b,), generator=g, dtype=torch.int64)
+                      .to(torch.int32))
+        q.append(_normal(g, (b, cfg.h, cfg.dh), cfg.dtype))
+        k_new.append(_normal(g, (b, cfg.G, cfg.dh), cfg.dtype))
+        v_new.append(_normal(g, (b, cfg.G, cfg.dh), cfg.dtype))
+    return dict(K=K, V=V, lens=lens, parent=torch.stack(parent), q=torch.stack(q),
+                k_new=torch.stack(k_new), v_new=torch.stack(v_new))
 
 
 def prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None, b: Optional[int] = None,

@@ -41,6 +41,7 @@ def lib(libmqa_path):
     L.mqa_decode_ex.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P]
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
+    L.mqa_kv_reorder.argtypes = [CP, P, P, I32, P, P]
     return L
 
 
@@ -56,7 +57,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
         "mqa_decode_ex", "mqa_decode_workspace_size",
-        "mqa_kv_append", "mqa_prefill_causal", "mqa_strerror"])
+        "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib, libmqa_path):
@@ -72,7 +73,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 200
+    assert q.abi_version() == 201
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -171,3 +172,22 @@ def test_check_lens_argument_errors(lib):
     assert lib.mqa_check_lens(None, 3, 10, None) == ENULL
     assert lib.mqa_check_lens(FAKE, -1, 10, None) == ESHAPE
     assert lib.mqa_check_lens(None, 0, 10, None) == OK
+
+
+def test_reorder_rejects_bad_arguments_before_launching(lib):
+    r = lib.mqa_kv_reorder
+
+    def call(c=None, lens=FAKE, parent=FAKE, beam=4):
+        c = c if c is not None else cache(b=8)
+        return r(ctypes.byref(c), lens, parent, beam, None, None)
+
+    assert r(None, FAKE, FAKE, 4, None, None) == ENULL
+    assert call(lens=None) == ENULL
+    assert call(parent=None) == ENULL
+    assert call(c=cache(b=8, k=None)) == ENULL
+    assert call(beam=0) == ESHAPE
+    assert call(beam=3) == ESHAPE                       # does not divide b = 8
+    assert call(c=cache(b=32), beam=32) == ESHAPE       # beam > 16
+    assert call(c=cache(b=8, dh=96)) == EDHEAD
+    assert call(c=cache(b=8, k=FAKE_MIS)) == EALIGN
+    assert call(c=cache(b=0)) == OK                     # nothing to do, nothing launched
