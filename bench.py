@@ -266,6 +266,97 @@ def prefill_result(cfg, steps, torch, mqa, R=2):
                 causal_flops=flops)
 
 
+# --------------------------------------------------------------------------- beam
+
+
+def beam_result(cfg, steps, torch, mqa, R=4):
+    """Beam step = mqa_kv_reorder (random parents, ~3/4 of the rows move)
+    followed by the fused append + decode, over R rotated caches, replayed
+    from a HIP graph.  Bytes: the decode's K/V of every hypothesis plus the
+    reorder's moved rows, read and written."""
+    dev = torch.device("cuda")
+    b, h, G, dh, m_cap, beam = cfg.b, cfg.h, cfg.G, cfg.dh, cfg.m_cap, cfg.beam
+    elem = 2 if cfg.dtype == torch.bfloat16 else 4
+    row = G * dh * elem
+    copies, per_src, moved = [], [], []
+    for r in range(R):
+        gg = torch.Generator(device=dev).manual_seed(cfg.seed * 1000 + r)
+        gc = torch.Generator().manual_seed(cfg.seed * 1000 + r)
+        K = torch.randn(b, m_cap, G, dh, generator=gg, device=dev).to(cfg.dtype)
+        V = torch.randn(b, m_cap, G, dh, generator=gg, device=dev).to(cfg.dtype)
+        src_lens = torch.randint(cfg.lens_lo, cfg.lens_hi + 1, (cfg.sources,), generator=gc,
+                                 dtype=torch.int64)
+        parent = torch.randint(0, beam, (b,), generator=gc, dtype=torch.int64).to(torch.int32)
+        c = dict(K=K, V=V, lens=src_lens.repeat_interleave(beam).to(torch.int32).to(dev),
+                 parent=parent.to(dev),
+                 q=torch.randn(b, h, dh, generator=gg, device=dev).to(cfg.dtype),
+                 kn=torch.randn(b, G, dh, generator=gg, device=dev).to(cfg.dtype),
+                 vn=torch.randn(b, G, dh, generator=gg, device=dev).to(cfg.dtype))
+        copies.append(c)
+        per_src.append(src_lens.tolist())
+        # moved rows per source (a moved row copies its source's length)
+        moved.append([sum(1 for i in range(s_i * beam, (s_i + 1) * beam)
+                          if int(parent[i]) != i % beam) for s_i in range(cfg.sources)])
+    out = torch.empty(b, h, dh, dtype=cfg.dtype, device=dev)
+    ws = mqa.workspace_for(h, copies[0]["K"])
+    dsteps = [mqa.DecodeStep(c["q"], c["K"], c["V"], c["lens"], cfg.scale, out=out,
+                             workspace=ws, k_new=c["kn"], v_new=c["vn"]) for c in copies]
+
+    def step(r):
+        c = copies[r]
+        mqa.kv_reorder(c["K"], c["V"], c["lens"], c["parent"], beam)
+        dsteps[r]()
+
+    appends = [0] * R
+
+    def step_bytes(r, n_app):
+        # hypotheses of a source share its length before and after every step
+        rd = mv = 0
+        for s_i, L0 in enumerate(per_src[r]):
+            L_pre = min(L0 + n_app, m_cap)        # length entering this step
+            L = min(L_pre + 1, m_cap)             # after the append
+            rd += beam * L * row * 2              # decode reads K and V
+            mv += moved[r][s_i] * L_pre
+        return rd, 2 * 2 * mv * row               # moved rows: read + write, K and V
+
+    for i in range(2 * R):                         # warm-up
+        step(i % R)
+        appends[i % R] += 1
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for r in range(R):
+                step(r)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    n_rep = max(1, math.ceil(steps / R))
+    # the capture itself ran one step per copy
+    for r in range(R):
+        appends[r] += 1
+    kv = mvb = 0
+    for k in range(n_rep):
+        for r in range(R):
+            a, m = step_bytes(r, appends[r] + k)
+            kv += a
+            mvb += m
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    n = n_rep * R
+    return dict(ms_per_step=1e3 * dt / n, steps_per_s=n / dt,
+                us_per_output_token=1e6 * dt / n / cfg.sources,
+                kv_gbps=kv / dt / 1e9, reorder_gbps=mvb / dt / 1e9,
+                total_gbps=(kv + mvb) / dt / 1e9,
+                total_frac_of_peak=(kv + mvb) / dt / 1e9 / HBM_PEAK_GBPS,
+                moved_rows_per_step=sum(sum(m) for m in moved) / R, hypotheses=b)
+
+
 # --------------------------------------------------------------------------- cpu baseline
 
 
@@ -377,6 +468,10 @@ def main():
         log("c5 causal prefill")
         extra["c5_prefill_b4_n4096"] = {k: round(v, 4) if isinstance(v, float) else v
                                         for k, v in prefill_result(W.C5, 10, torch, mqa).items()}
+        torch.cuda.empty_cache()
+        log("beam-4 step: reorder + fused append + decode, 16 sources x 4 beams")
+        extra["beam4_b16x4_ragged8k"] = {k: round(v, 4) if isinstance(v, float) else v
+                                         for k, v in beam_result(W.BEAM4, 96, torch, mqa).items()}
         torch.cuda.empty_cache()
 
     cpu = None
