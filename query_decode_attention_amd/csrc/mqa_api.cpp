@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "mqa_internal.h"
+#include "mqa_reorder.h"
 
 namespace mqa {
 

@@ -52,18 +52,6 @@ struct PrefillParams {
   float scale;
 };
 
-// Beam reorder of the cache (in place).
-constexpr int kMaxBeam = 16;
-struct ReorderParams {
-  char* k;
-  char* v;
-  int32_t* lens;
-  const int32_t* parent;  // beam-local parent of every hypothesis
-  int32_t* err_flag;      // nullable
-  int b, m_cap, beam;
-  int row_bytes;          // G * d_h * element size
-};
-
 // Size in bytes of one split-K partial record for hg heads of width dh.
 size_t decode_record_bytes(int hg, int dh);
 // Byte offset of the first record in the workspace (after the schedule header).
@@ -76,7 +64,6 @@ size_t decode_workspace_bytes(int b, int h, int G, int dh, int m_cap);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
-hipError_t launch_kv_reorder(const ReorderParams& p, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int current_device_cus(int* device_out);

@@ -19,7 +19,7 @@
 // lens is rewritten by a second, one-workgroup kernel afterwards (every block
 // of the first kernel reads the old lengths).
 #include "mqa_device.h"
-#include "mqa_internal.h"
+#include "mqa_reorder.h"
 
 namespace mqa {
 
