@@ -55,6 +55,9 @@ def _load():
         lib.oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, D, I, P, I]
         lib.oracle_decode_weights.argtypes = [I, I, I, I, I, I, P, P, P, P, D, I, I, I, P]
         lib.oracle_prefill.argtypes = [I, I, I, I, I, I, P, P, P, D, P, ctypes.c_int64, P, I]
+        L64 = ctypes.c_int64
+        lib.oracle_attend.argtypes = [I, I, I, I, I, I, I, P, P, P, D, P, L64, L64, L64, P, L64,
+                                      P, I]
         for f in (lib.oracle_kv_append, lib.oracle_decode, lib.oracle_decode_weights,
                   lib.oracle_prefill):
             f.restype = I
@@ -198,4 +201,43 @@ def prefill(Q, K, V, scale, rows=None, nthreads=None) -> np.ndarray:
                                 rp, nr, _ptr(out), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments")
+    return out.reshape(b, n, h, dh) if rows is None else out
+
+
+def attend(Q, K, V, scale, mask=None, strides=None, rows=None, nthreads=None) -> np.ndarray:
+    """fp64 attention over a fixed memory.  Q [b,n,h,dh]; K,V [b,m,G,dh].
+
+    mask: optional float32 array (any shape) read at
+    b*sb + i*sh + t*sn + j with strides=(sb, sh, sn) in elements; with
+    strides None the mask must be a dense [b, h, n, m] array.
+    rows: as in prefill; returns [nrows, h, dh] or [b, n, h, dh].
+    """
+    Qa, dt = _raw(Q)
+    Ka, dk = _raw(K)
+    Va, dv = _raw(V)
+    assert dt == dk == dv
+    b, n, h, dh = Qa.shape
+    m, G = Ka.shape[1], Ka.shape[2]
+    assert Ka.shape == (b, m, G, dh) and Va.shape == Ka.shape
+    mp, sb, sh, sn = None, 0, 0, 0
+    if mask is not None:
+        mk = mask.numpy() if hasattr(mask, "numpy") else mask
+        mk = np.ascontiguousarray(mk, dtype=np.float32)
+        if strides is None:
+            assert mk.shape == (b, h, n, m)
+            strides = (h * n * m, n * m, m)
+        sb, sh, sn = (int(x) for x in strides)
+        mp = _ptr(mk)
+    if rows is None:
+        out = np.zeros((b * n, h, dh), dtype=np.float64)
+        rp, nr = None, b * n
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.zeros((r.size, h, dh), dtype=np.float64)
+        rp, nr = _ptr(r), r.size
+    rc = _load().oracle_attend(dt, b, n, m, h, G, dh, _ptr(Qa), _ptr(Ka), _ptr(Va), float(scale),
+                               mp, sb, sh, sn, rp, nr, _ptr(out),
+                               int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_attend rejected its arguments")
     return out.reshape(b, n, h, dh) if rows is None else out

@@ -300,3 +300,88 @@ int oracle_prefill(int dtype, int b, int n, int h, int G, int dh,
   free(jobs);
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------ attend */
+
+typedef struct {
+  int dtype, b, n, m, h, G, dh;
+  const void *Q, *K, *V;
+  const float* mask;
+  int64_t sb, sh, sn;
+  double scale;
+  const int64_t* rows;
+  int64_t r_begin, r_end;
+  double* O;
+} attend_job;
+
+static void* attend_worker(void* arg) {
+  attend_job* J = (attend_job*)arg;
+  double* x = (double*)malloc(sizeof(double) * (size_t)J->m);
+  for (int64_t k = J->r_begin; k < J->r_end; ++k) {
+    const int64_t r = J->rows ? J->rows[k] : k;
+    const int bi = (int)(r / J->n), t = (int)(r % J->n);
+    for (int i = 0; i < J->h; ++i) {
+      const int g = i / (J->h / J->G);
+      const int64_t qoff = (((int64_t)bi * J->n + t) * J->h + i) * J->dh;
+      /* logits + additive mask over the whole memory */
+      double mx = -INFINITY;
+      for (int j = 0; j < J->m; ++j) {
+        const int64_t koff = (((int64_t)bi * J->m + j) * J->G + g) * J->dh;
+        double s = 0.0;
+        for (int r2 = 0; r2 < J->dh; ++r2)
+          s += elem(J->dtype, J->Q, qoff + r2) * elem(J->dtype, J->K, koff + r2);
+        s *= J->scale;
+        if (J->mask) s += (double)J->mask[bi * J->sb + i * J->sh + t * J->sn + j];
+        x[j] = s;
+        if (x[j] > mx) mx = x[j];
+      }
+      double* out = J->O + (k * J->h + i) * J->dh;
+      if (mx == -INFINITY) {                   /* every key hidden: zeros */
+        for (int d = 0; d < J->dh; ++d) out[d] = 0.0;
+        continue;
+      }
+      double z = 0.0;
+      for (int j = 0; j < J->m; ++j) {
+        x[j] = exp(x[j] - mx);                 /* exp(-inf) = 0 */
+        z += x[j];
+      }
+      for (int d = 0; d < J->dh; ++d) {
+        double acc = 0.0;
+        for (int j = 0; j < J->m; ++j) {
+          const int64_t voff = (((int64_t)bi * J->m + j) * J->G + g) * J->dh;
+          acc += (x[j] / z) * elem(J->dtype, J->V, voff + d);
+        }
+        out[d] = acc;
+      }
+    }
+  }
+  free(x);
+  return NULL;
+}
+
+int oracle_attend(int dtype, int b, int n, int m, int h, int G, int dh,
+                  const void* Q, const void* K, const void* V, double scale,
+                  const float* mask, int64_t sb, int64_t sh, int64_t sn,
+                  const int64_t* rows, int64_t nrows, double* O, int nthreads) {
+  if (check_common(dtype, b, h, G, dh) != ORACLE_OK || n <= 0 || m <= 0) return ORACLE_EINVAL;
+  if (mask && (sb < 0 || sh < 0 || sn < 0)) return ORACLE_EINVAL;
+  const int64_t total = rows ? nrows : (int64_t)b * n;
+  if (rows)
+    for (int64_t k = 0; k < nrows; ++k)
+      if (rows[k] < 0 || rows[k] >= (int64_t)b * n) return ORACLE_EINVAL;
+  if (total == 0) return ORACLE_OK;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > total) nthreads = (int)total;
+  attend_job* jobs = (attend_job*)calloc((size_t)nthreads, sizeof(attend_job));
+  for (int t = 0; t < nthreads; ++t) {
+    attend_job* J = &jobs[t];
+    J->dtype = dtype; J->b = b; J->n = n; J->m = m; J->h = h; J->G = G; J->dh = dh;
+    J->Q = Q; J->K = K; J->V = V; J->scale = scale; J->rows = rows; J->O = O;
+    J->mask = mask; J->sb = sb; J->sh = sh; J->sn = sn;
+    J->r_begin = total * t / nthreads;
+    J->r_end = total * (t + 1) / nthreads;
+  }
+  run_jobs(attend_worker, jobs, sizeof(attend_job), nthreads);
+  free(jobs);
+  return ORACLE_OK;
+}

@@ -24,6 +24,7 @@
  *   k_new, v_new  [b][G][dh]
  *   lens          int32 [b]
  *   Q, O prefill  [b][n][h][dh];  K, V prefill [b][n][G][dh]
+ *   attend: Q, O [b][n][h][dh]; K, V memory [b][m][G][dh]
  */
 #ifndef MQA_ORACLE_H
 #define MQA_ORACLE_H
@@ -82,6 +83,20 @@ int oracle_decode_weights(int dtype, int b, int h, int G, int dh, int m_cap,
 int oracle_prefill(int dtype, int b, int n, int h, int G, int dh,
                    const void* Q, const void* K, const void* V, double scale,
                    const int64_t* rows, int64_t nrows, double* O, int nthreads);
+
+/* Attention of n queries per sequence over a fixed memory of m positions,
+ * with no causal structure and an optional additive mask (the paper review's
+ * section 2.3 batched pseudocode: softmax(logits + mask) over the memory
+ * axis; the study notes' section 6.1: multi-query attention also serves
+ * encoder-decoder attention):
+ *   x_j = scale * Q[b,t,i,:].K[b,j,g(i),:] + mask[b*sb + i*sh + t*sn + j],  j < m
+ *   O[b,t,i,:] = sum_j softmax(x)_j V[b,j,g(i),:]
+ * Q [b][n][h][dh]; K, V [b][m][G][dh]; mask fp32 (NULL: none); a row whose
+ * every x_j is -inf yields zeros.  rows / nrows / O as in oracle_prefill. */
+int oracle_attend(int dtype, int b, int n, int m, int h, int G, int dh,
+                  const void* Q, const void* K, const void* V, double scale,
+                  const float* mask, int64_t sb, int64_t sh, int64_t sn,
+                  const int64_t* rows, int64_t nrows, double* O, int nthreads);
 
 #ifdef __cplusplus
 }

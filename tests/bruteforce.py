@@ -58,3 +58,28 @@ def prefill(Q, K, V, scale):
                 vals = [list(V[bi, j, g]) for j in range(t + 1)]
                 out[bi, t, i] = attend(list(Q[bi, t, i]), keys, vals, scale)[0]
     return out
+
+
+def memory(Q, K, V, scale, mask=None):
+    """Non-causal attention over a memory with an additive mask (paper review
+    section 2.3: softmax(logits + mask)).  Q [b,n,h,dh], K/V [b,m,G,dh],
+    mask [b,h,n,m] or None; a row whose logits are all -inf gives zeros."""
+    b, n, h, dh = Q.shape
+    m, G = K.shape[1], K.shape[2]
+    hg = h // G
+    out = np.zeros((b, n, h, dh))
+    for bi in range(b):
+        for t in range(n):
+            for i in range(h):
+                g = i // hg
+                logits = [scale * math.fsum(x * y for x, y in zip(Q[bi, t, i], K[bi, j, g]))
+                          + (0.0 if mask is None else float(mask[bi, i, t, j]))
+                          for j in range(m)]
+                top = max(logits)
+                if top == -math.inf:
+                    continue
+                e = [math.exp(x - top) for x in logits]
+                z = math.fsum(e)
+                for d in range(dh):
+                    out[bi, t, i, d] = math.fsum(ej / z * V[bi, j, g, d] for j, ej in enumerate(e))
+    return out

@@ -449,3 +449,85 @@ def test_oracle_rejects_bad_arguments():
     K = rand((1, 4, 2, 8), 2)
     with pytest.raises(ValueError):
         oracle.decode(q, K, K, np.array([4], np.int32), 1.0)  # G=2 does not divide h=3
+
+
+# ---------------------------------------------------------------- attend (memory, mask)
+
+
+def _memory_case(dtype, b=2, n=3, m=9, h=4, G=2, dh=64, seed=170):
+    Q = rand((b, n, h, dh), seed, dtype)
+    K = rand((b, m, G, dh), seed + 1, dtype)
+    V = rand((b, m, G, dh), seed + 2, dtype)
+    return Q, K, V
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_attend_with_mask_against_bruteforce(dtype):
+    b, n, m, h = 2, 3, 9, 4
+    Q, K, V = _memory_case(dtype)
+    g = np.random.default_rng(171)
+    mask = g.normal(0, 2, size=(b, h, n, m)).astype(np.float32)
+    mask[0, 1, 2, :5] = -np.inf
+    mask[1, 3, 0, :] = -np.inf                        # a fully hidden row
+    got = oracle.attend(Q, K, V, 0.3, mask)
+    want = bruteforce.memory(f64(Q), f64(K), f64(V), 0.3, mask)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13)
+    assert not got[1, 0, 3].any()
+    got0 = oracle.attend(Q, K, V, 0.3)
+    assert np.allclose(got0, bruteforce.memory(f64(Q), f64(K), f64(V), 0.3), rtol=1e-12,
+                       atol=1e-13)
+
+
+def test_attend_key_padding_mask_is_decode_with_lens():
+    """n = 1 and -inf on keys j >= L_b (a [b, m] key-padding mask broadcast
+    over heads and queries through zero strides) is decode over L_b rows."""
+    b, m, h, G, dh = 3, 11, 4, 1, 64
+    q = rand((b, h, dh), 175, torch.bfloat16)
+    K = rand((b, m, G, dh), 176, torch.bfloat16)
+    V = rand((b, m, G, dh), 177, torch.bfloat16)
+    lens = np.array([11, 4, 1], np.int32)
+    pad = np.where(np.arange(m)[None, :] < lens[:, None], 0.0, -np.inf).astype(np.float32)
+    got = oracle.attend(q[:, None], K, V, 0.125, pad, strides=(m, 0, 0))
+    want = oracle.decode(q, K, V, lens, 0.125)
+    assert np.allclose(got[:, 0], want, rtol=1e-13, atol=1e-15)
+
+
+def test_attend_causal_mask_is_prefill():
+    b, n, h, G, dh = 2, 6, 4, 2, 64
+    Q = rand((b, n, h, dh), 178, torch.bfloat16)
+    K = rand((b, n, G, dh), 179, torch.bfloat16)
+    V = rand((b, n, G, dh), 180, torch.bfloat16)
+    causal = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], 0.0, -np.inf)
+    mask = np.broadcast_to(causal.astype(np.float32), (b, h, n, n))
+    got = oracle.attend(Q, K, V, 0.125, mask)
+    assert np.allclose(got, oracle.prefill(Q, K, V, 0.125), rtol=1e-13, atol=1e-15)
+
+
+def test_attend_hidden_key_equals_removed_key():
+    Q, K, V = _memory_case(torch.float32)
+    b, n, h = 2, 3, 4
+    m = K.shape[1]
+    mask = np.zeros((b, h, n, m), np.float32)
+    mask[:, :, :, 4] = -np.inf
+    keep = [j for j in range(m) if j != 4]
+    got = oracle.attend(Q, K, V, 0.2, mask)
+    want = oracle.attend(Q, K[:, keep].contiguous(), V[:, keep].contiguous(), 0.2)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+def test_attend_mask_shift_invariance_and_one_hot():
+    Q, K, V = _memory_case(torch.float32)
+    b, n, h = 2, 3, 4
+    m = K.shape[1]
+    g = np.random.default_rng(181)
+    # dyadic values, so that the shifted mask is exact in fp32
+    mask = (g.integers(-16, 17, size=(b, h, n, m)) / 8.0).astype(np.float32)
+    a = oracle.attend(Q, K, V, 0.2, mask)
+    c = oracle.attend(Q, K, V, 0.2, mask + np.float32(37.0))
+    assert np.allclose(a, c, rtol=1e-11, atol=1e-12)
+    hot = np.zeros((b, h, n, m), np.float32)
+    hot[:, :, :, 6] = 1e4                              # one key dominates completely
+    o = oracle.attend(Q, K, V, 0.2, hot)
+    Vd = f64(V)
+    for i in range(h):
+        assert np.array_equal(o[:, :, i], np.broadcast_to(Vd[:, None, 6, i // 2], o[:, :, i].shape))
