@@ -164,6 +164,25 @@ int mqa_prefill_causal(const void* Q, const void* K, const void* V, int32_t b, i
                        int32_t h, int32_t G, int32_t d_h, int32_t dtype, float scale,
                        const mqa_cache* cache, int32_t* lens, void* O, void* stream);
 
+/* mqa_attend -- n queries per sequence attending over a fixed memory of m
+ * positions with no causal structure, as in encoder-decoder attention (the
+ * study notes' section 6.1: the multi-query layers replace encoder-decoder
+ * attention too; the paper review's section 2.3 batched form, weights =
+ * softmax(logits + mask)):
+ *     O[b,t,i,:] = sum_j w_j V[b,j,g(i),:],
+ *     w = softmax_j over j < m of (scale * Q[b,t,i,:].K[b,j,g(i),:] + mask(b,i,t,j))
+ *   Q, O  : device [b][n][h][d_h];  K, V : device [b][m][G][d_h] (the memory).
+ *   mask  : optional device fp32, 4-byte aligned; mask(b,i,t,j) is read at
+ *           mask[b*mask_sb + i*mask_sh + t*mask_sn + j] (element strides >= 0,
+ *           key index contiguous; a stride of 0 broadcasts: the pages' full
+ *           [b][h][n][m] mask has strides (h*n*m, n*m, m), a key-padding mask
+ *           [b][m] has (m, 0, 0)).  NULL: no mask.  -inf hides a key; a row
+ *           whose every key is hidden gives o = 0.
+ *   No cache is touched.  One launch on `stream`. */
+int mqa_attend(const void* Q, const void* K, const void* V, int32_t b, int32_t n, int32_t m,
+               int32_t h, int32_t G, int32_t d_h, int32_t dtype, float scale, const float* mask,
+               int64_t mask_sb, int64_t mask_sh, int64_t mask_sn, void* O, void* stream);
+
 /* Debug helper: synchronises `stream`, copies lens to the host and returns
  * MQA_ERR_LENS if any lens[b] lies outside [0, m_cap], else MQA_OK. */
 int mqa_check_lens(const int32_t* lens, int32_t b, int32_t m_cap, void* stream);

@@ -33,7 +33,7 @@ _DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
 
 # Symbols include/mqa.h declares (tests check the library exports each one).
 EXPORTED = ("mqa_kv_append", "mqa_kv_reorder", "mqa_decode_workspace_size",
-            "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal",
+            "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal", "mqa_attend",
             "mqa_check_lens", "mqa_strerror", "mqa_abi_version")
 
 
@@ -68,6 +68,8 @@ def _load():
         "mqa_decode_ex": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P], ctypes.c_int),
         "mqa_prefill_causal": ([P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P],
                                ctypes.c_int),
+        "mqa_attend": ([P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, ctypes.c_int64,
+                        ctypes.c_int64, ctypes.c_int64, P, P], ctypes.c_int),
         "mqa_check_lens": ([P, I32, I32, P], ctypes.c_int),
         "mqa_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "mqa_abi_version": ([], ctypes.c_int),
@@ -282,6 +284,40 @@ def prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=No
     _check("mqa_prefill_causal", _lib.mqa_prefill_causal(
         _ptr(Q), _ptr(K), _ptr(V), b, n, h, G, dh, _DTYPES[Q.dtype], float(scale), cp,
         _ptr(lens), _ptr(out), _stream(dev)))
+    return out
+
+
+def attend(Q, K, V, scale, mask=None, out=None):
+    """Attention of Q [b,n,h,d_h] over a fixed memory K, V [b,m,G,d_h] with no
+    causal structure: O = softmax(scale * Q K^T + mask) V per head, head i
+    reading K/V group i // (h/G).
+
+    mask: optional float32 tensor on the same device, any shape that
+    broadcasts to [b, h, n, m] with the key dimension contiguous (a [b,1,1,m]
+    key-padding mask or a full [b,h,n,m] one); -inf hides a key, and a row
+    whose every key is hidden gives zeros."""
+    if out is None:
+        out = torch.empty_like(Q)
+    dev = _dev(Q, K, V, out, mask)
+    b, n, h, dh = Q.shape
+    if K.dim() != 4 or K.shape[0] != b or K.shape[3] != dh or V.shape != K.shape:
+        raise ValueError("K / V must be [b, m, G, d_h] matching Q")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype or out.dtype != Q.dtype or out.shape != Q.shape:
+        raise ValueError("Q, K, V and out must share one dtype and Q's shape")
+    if Q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {Q.dtype}")
+    m, G = K.shape[1], K.shape[2]
+    sb = sh = sn = 0
+    if mask is not None:
+        if mask.dtype != torch.float32:
+            raise ValueError("mask must be float32")
+        mask = mask.expand(b, h, n, m)
+        if mask.stride(3) != 1:
+            raise ValueError("the mask's key dimension must be contiguous")
+        sb, sh, sn = mask.stride(0), mask.stride(1), mask.stride(2)
+    _check("mqa_attend", _lib.mqa_attend(
+        _ptr(Q), _ptr(K), _ptr(V), b, n, m, h, G, dh, _DTYPES[Q.dtype], float(scale),
+        _ptr(mask), sb, sh, sn, _ptr(out), _stream(dev)))
     return out
 
 

@@ -12,6 +12,7 @@
 
 #include "mqa_internal.h"
 #include "mqa_reorder.h"
+#include "mqa_attend.h"
 
 namespace mqa {
 
@@ -76,7 +77,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MQA_OK : MQA_ERR_LAUN
 
 extern "C" {
 
-int mqa_abi_version(void) { return 201; }
+int mqa_abi_version(void) { return 202; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -228,6 +229,43 @@ int mqa_prefill_causal(const void* Q, const void* K, const void* V, int32_t b, i
   p.m_cap = cache ? cache->m_cap : n;
   p.scale = scale;
   return launch_status(mqa::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+int mqa_attend(const void* Q, const void* K, const void* V, int32_t b, int32_t n, int32_t m,
+               int32_t h, int32_t G, int32_t d_h, int32_t dtype, float scale, const float* mask,
+               int64_t mask_sb, int64_t mask_sh, int64_t mask_sn, void* O, void* stream) {
+  if (dtype != MQA_F32 && dtype != MQA_BF16) return MQA_ERR_DTYPE;
+  if (d_h != 64 && d_h != 128) return MQA_ERR_DHEAD;
+  if (b < 0 || n < 1 || m < 1) return MQA_ERR_SHAPE;
+  int rc = check_heads(h, G);
+  if (rc != MQA_OK) return rc;
+  if ((int64_t)b * G * ((n + 7) / 8) >= ((int64_t)1 << 31)) return MQA_ERR_SHAPE;
+  if (mask && (mask_sb < 0 || mask_sh < 0 || mask_sn < 0)) return MQA_ERR_SHAPE;
+  if (b == 0) return MQA_OK;
+  if (!Q || !K || !V || !O) return MQA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return MQA_ERR_ALIGN;
+  if (mask && (reinterpret_cast<uintptr_t>(mask) & 3u)) return MQA_ERR_ALIGN;
+  mqa::AttendParams a;
+  a.base.Q = Q;
+  a.base.K = K;
+  a.base.V = V;
+  a.base.O = O;
+  a.base.cache_k = a.base.cache_v = nullptr;
+  a.base.lens = nullptr;
+  a.base.b = b;
+  a.base.n = n;
+  a.base.h = h;
+  a.base.G = G;
+  a.base.dh = d_h;
+  a.base.dtype = dtype;
+  a.base.m_cap = m;
+  a.base.scale = scale;
+  a.m = m;
+  a.mask = mask;
+  a.msb = mask_sb;
+  a.msh = mask_sh;
+  a.msn = mask_sn;
+  return launch_status(mqa::launch_attend(a, static_cast<hipStream_t>(stream)));
 }
 
 int mqa_check_lens(const int32_t* lens, int32_t b, int32_t m_cap, void* stream) {

@@ -198,18 +198,21 @@ template <> struct PvOps<float> {
   }
 };
 
-// Online-softmax step: scale the raw scores, mask positions beyond this
-// lane's limit (pos > lim) unless FULL, update (m, l), rescale o, and return
-// the unnormalised probabilities p (exp2 of logit minus the new max).  For
-// bf16 the probabilities are rounded to bf16 before they are summed, so the
+// Online-softmax step: scale the raw scores, add the additive mask `bias`
+// (already in log2 units) when BIAS, mask positions beyond this lane's limit
+// (pos > lim) unless FULL, update (m, l), rescale o, and return the
+// unnormalised probabilities p (exp2 of logit minus the new max).  For bf16
+// the probabilities are rounded to bf16 before they are summed, so the
 // normaliser l is the sum of exactly the weights the PV product uses.
-template <typename T, int ND, bool FULL>
+template <typename T, int ND, bool FULL, bool BIAS = false>
 __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s, float scale_log2,
-                                             int pos0, int lim, int half, float (&p)[16]) {
+                                             int pos0, int lim, int half, float (&p)[16],
+                                             const float* bias = nullptr) {
   float t[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     t[r] = s[r] * scale_log2;
+    if constexpr (BIAS) t[r] += bias[r];
     if (!FULL && pos0 + d_row(r, half) > lim) t[r] = kNegInf;
   }
   float mt = t[0];

@@ -1,7 +1,11 @@
-// mqa_prefill.hip -- gfx950 causal prefill for MQA/GQA:
-//   O[b,t,i,:] = softmax_{j<=t}(scale * Q[b,t,i,:] . K[b,j,g(i),:]) V[b,j,g(i),:]
-// (study notes section 1: O = softmax(QK^T/sqrt(d_h) + M) V, M = -inf above the
-// diagonal; paper review section 2.3 batched form with an additive mask).
+// mqa_prefill.hip -- gfx950 batched attention of n queries per sequence:
+//   causal prefill:  O[b,t,i,:] = softmax_{j<=t}(scale * Q[b,t,i,:] . K[b,j,g(i),:]) V[b,j,g(i),:]
+//   (study notes section 1: O = softmax(QK^T/sqrt(d_h) + M) V, M = -inf above
+//   the diagonal), and
+//   attention over a fixed memory of m positions with an optional additive
+//   mask, no causal structure (encoder-decoder attention; paper review
+//   section 2.3 batched form, weights = softmax(logits + mask)):
+//                    O[b,t,i,:] = softmax_{j<m}(scale * Q[b,t,i,:] . K[b,j,g(i),:] + mask[b,i,t,j]) V[b,j,g(i),:]
 //
 // Columns.  A wave owns 32 query columns = rpw consecutive rows x hgp head
 // slots of one group (hgp = h/G rounded up to a power of two), so with MQA
@@ -17,6 +21,7 @@
 // blocks are launched last-row-first so the longest causal rows start early.
 #include "mqa_device.h"
 #include "mqa_internal.h"
+#include "mqa_attend.h"
 
 namespace mqa {
 
@@ -25,11 +30,13 @@ struct PrefillArgs {
   const char* K;
   const char* V;
   char* O;
-  int b, n, h, G, hg, hgp, rpw, nrb;
+  const float* mask;        // non-causal only; nullable
+  int64_t msb, msh, msn;    // mask element strides over (b, head, query row)
+  int b, n, m, h, G, hg, hgp, rpw, nrb;  // m: key/value positions (= n when causal)
   float scale_log2;
 };
 
-template <typename T, int DH, int NW>
+template <typename T, int DH, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
@@ -50,11 +57,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int r_begin = rb * rows_per_block;
   if (r_begin >= a.n) return;
   const int r_end = min(a.n, r_begin + rows_per_block);
-  const int ntiles = (r_end - 1) / kTileRows + 1;
+  const int ntiles = CAUSAL ? (r_end - 1) / kTileRows + 1 : (a.m + kTileRows - 1) / kTileRows;
 
   const int w_row0 = r_begin + wave * a.rpw;
   const int w_last = min(a.n - 1, w_row0 + a.rpw - 1);
-  const int w_tiles = (w_row0 < a.n) ? w_last / kTileRows + 1 : 0;
+  const int w_tiles = (w_row0 < a.n) ? (CAUSAL ? w_last / kTileRows + 1 : ntiles) : 0;
   const int crow = w_row0 + col / a.hgp;
   const int chead = col % a.hgp;
   const bool col_ok = crow < a.n && chead < a.hg;
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   SelOps<T> sel;
   sel.init(col, half);
   const size_t rs = (size_t)a.G * DH * sizeof(T);
-  const size_t seq_off = ((size_t)bi * a.n * a.G + (size_t)g) * DH * sizeof(T);
+  const size_t seq_off = ((size_t)bi * a.m * a.G + (size_t)g) * DH * sizeof(T);
   const char* kseq = a.K + seq_off;
   const char* vseq = a.V + seq_off;
 
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   auto issue = [&](int tile) {
     const int pos = tile * kTileRows + col;
-    const bool valid = pos < a.n;
+    const bool valid = pos < a.m;
     if (v_wave) {
       const char* p = vseq + (size_t)pos * rs;
 #pragma unroll
@@ -116,6 +123,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
 
+  // additive mask row of this lane's column (non-causal only)
+  const float* mrow = nullptr;
+  if (!CAUSAL && a.mask && col_ok)
+    mrow = a.mask + (int64_t)bi * a.msb + (int64_t)(g * a.hg + chead) * a.msh + (int64_t)crow * a.msn;
+  constexpr float kLog2e = 1.4426950408889634f;
+
   WaveState<ND> st;
   st.reset();
   issue(0);
@@ -131,10 +144,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       const f32x16 s = tile_scores<T, NQ>(kr, qr);
       const int pos0 = it * kTileRows;
       float p[16];
-      if (pos0 + kTileRows - 1 <= w_row0)
-        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
-      else
-        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
+      if constexpr (CAUSAL) {
+        if (pos0 + kTileRows - 1 <= w_row0)
+          softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
+        else
+          softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
+      } else if (a.mask) {
+        float bias[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = pos0 + d_row(r, half);
+          bias[r] = (mrow && j < a.m) ? mrow[j] * kLog2e : 0.f;
+        }
+        softmax_tile<T, ND, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
+      } else {
+        if (pos0 + kTileRows <= a.m)
+          softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+        else
+          softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+      }
       PvOps<T> pv;
       pv.set(p);
 #pragma unroll
@@ -149,7 +177,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   const float l_tot = st.l + xor32(st.l);
   if (col_ok) {
-    const float inv = 1.0f / l_tot;
+    // a row whose every key is masked out gets zeros (as an empty decode row)
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     T* op = reinterpret_cast<T*>(a.O) + (((size_t)bi * a.n + crow) * a.h + (size_t)g * a.hg + chead) * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -182,6 +211,31 @@ __global__ void prefill_cache_copy_kernel(const char* K, const char* V, char* ck
 namespace {
 constexpr int kPrefillWaves = 8;
 
+// Row blocks of NW * rpw query rows per (sequence, group).
+PrefillArgs row_blocks(const PrefillParams& p, int m) {
+  PrefillArgs a;
+  a.Q = (const char*)p.Q;
+  a.K = (const char*)p.K;
+  a.V = (const char*)p.V;
+  a.O = (char*)p.O;
+  a.mask = nullptr;
+  a.msb = a.msh = a.msn = 0;
+  a.b = p.b;
+  a.n = p.n;
+  a.m = m;
+  a.h = p.h;
+  a.G = p.G;
+  a.hg = p.h / p.G;
+  int hgp = 1;
+  while (hgp < a.hg) hgp *= 2;
+  a.hgp = hgp;
+  a.rpw = 32 / hgp;
+  const int rows_per_block = kPrefillWaves * a.rpw;
+  a.nrb = (p.n + rows_per_block - 1) / rows_per_block;
+  a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  return a;
+}
+
 template <typename T, int DH>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   const int row_bytes = p.G * p.dh * (int)sizeof(T);
@@ -197,25 +251,22 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  PrefillArgs a;
-  a.Q = (const char*)p.Q;
-  a.K = (const char*)p.K;
-  a.V = (const char*)p.V;
-  a.O = (char*)p.O;
-  a.b = p.b;
-  a.n = p.n;
-  a.h = p.h;
-  a.G = p.G;
-  a.hg = p.h / p.G;
-  int hgp = 1;
-  while (hgp < a.hg) hgp *= 2;
-  a.hgp = hgp;
-  a.rpw = 32 / hgp;
-  const int rows_per_block = kPrefillWaves * a.rpw;
-  a.nrb = (p.n + rows_per_block - 1) / rows_per_block;
-  a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  const PrefillArgs a = row_blocks(p, p.n);
   const size_t blocks = (size_t)p.b * p.G * a.nrb;
-  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true>), dim3((unsigned)blocks),
+                     dim3(kPrefillWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t launch_attend_t(const AttendParams& q, hipStream_t s) {
+  PrefillArgs a = row_blocks(q.base, q.m);
+  a.mask = q.mask;
+  a.msb = q.msb;
+  a.msh = q.msh;
+  a.msn = q.msn;
+  const size_t blocks = (size_t)q.base.b * q.base.G * a.nrb;
+  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false>), dim3((unsigned)blocks),
                      dim3(kPrefillWaves * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -228,6 +279,15 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   }
   if (p.dh == 128) return launch_prefill_t<float, 128>(p, s);
   return launch_prefill_t<float, 64>(p, s);
+}
+
+hipError_t launch_attend(const AttendParams& p, hipStream_t s) {
+  if (p.base.dtype == 1) {
+    if (p.base.dh == 128) return launch_attend_t<__bf16, 128>(p, s);
+    return launch_attend_t<__bf16, 64>(p, s);
+  }
+  if (p.base.dh == 128) return launch_attend_t<float, 128>(p, s);
+  return launch_attend_t<float, 64>(p, s);
 }
 
 }  // namespace mqa

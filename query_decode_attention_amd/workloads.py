@@ -105,6 +105,33 @@ class BeamConfig:
 BEAM4 = BeamConfig("beam4_b16x4_ragged8k", torch.bfloat16, sources=16, beam=4, h=32, G=1,
                    dh=128, m_cap=8192 + 256, lens_lo=1, lens_hi=8192, seed=1006)
 
+@dataclasses.dataclass(frozen=True)
+class MemoryConfig:
+    """Attention of n queries over a fixed memory of m positions (encoder-
+    decoder attention); each sequence's memory holds mem_len valid positions,
+    the rest hidden by a key-padding mask."""
+    name: str
+    dtype: torch.dtype
+    b: int
+    n: int
+    m: int
+    h: int
+    G: int
+    dh: int
+    mem_lo: int           # valid memory positions, uniform in [mem_lo, mem_hi]
+    mem_hi: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dh)
+
+
+# Encoder-decoder attention at the prefill's sizes (the study notes' section
+# 6.1: multi-query layers also serve encoder-decoder attention).
+ENCDEC = MemoryConfig("encdec_b4_n4096_m4096", torch.bfloat16, b=4, n=4096, m=4096, h=32, G=1,
+                      dh=128, mem_lo=2048, mem_hi=4096, seed=1007)
+
 DECODE_CONFIGS = {c.name: c for c in (C1, C2, C2_MHA, C3, C4)}
 PREFILL_CONFIGS = {C5.name: C5}
 
@@ -175,6 +202,26 @@ def beam_inputs(cfg: BeamConfig, steps: int = 1, seed: Optional[int] = None,
         v_new.append(_normal(g, (b, cfg.G, cfg.dh), cfg.dtype))
     return dict(K=K, V=V, lens=lens, parent=torch.stack(parent), q=torch.stack(q),
                 k_new=torch.stack(k_new), v_new=torch.stack(v_new))
+
+
+def memory_inputs(cfg: MemoryConfig, seed: Optional[int] = None, b: Optional[int] = None,
+                  n: Optional[int] = None, m: Optional[int] = None):
+    """CPU tensors Q [b,n,h,dh], K, V [b,m,G,dh], mem_len int32 [b] and the
+    key-padding mask float32 [b,1,1,m] (0 on valid positions, -inf past
+    mem_len).  Draw order Q, K, V, mem_len."""
+    b = cfg.b if b is None else b
+    n = cfg.n if n is None else n
+    m = cfg.m if m is None else m
+    g = torch.Generator("cpu").manual_seed(cfg.seed if seed is None else seed)
+    Q = _normal_chunked(g, (b, n, cfg.h, cfg.dh), cfg.dtype)
+    K = _normal_chunked(g, (b, m, cfg.G, cfg.dh), cfg.dtype)
+    V = _normal_chunked(g, (b, m, cfg.G, cfg.dh), cfg.dtype)
+    lo, hi = min(cfg.mem_lo, m), min(cfg.mem_hi, m)
+    mem_len = torch.randint(lo, hi + 1, (b,), generator=g, dtype=torch.int64).to(torch.int32)
+    mask = torch.zeros(b, 1, 1, m, dtype=torch.float32)
+    for bi in range(b):
+        mask[bi, 0, 0, int(mem_len[bi]):] = float("-inf")
+    return dict(Q=Q, K=K, V=V, mem_len=mem_len, mask=mask)
 
 
 def prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None, b: Optional[int] = None,

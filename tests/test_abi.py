@@ -42,6 +42,9 @@ def lib(libmqa_path):
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
     L.mqa_kv_reorder.argtypes = [CP, P, P, I32, P, P]
+    L64 = ctypes.c_int64
+    L.mqa_attend.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, L64, L64, L64,
+                             P, P]
     return L
 
 
@@ -57,7 +60,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
         "mqa_decode_ex", "mqa_decode_workspace_size",
-        "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_strerror"])
+        "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib, libmqa_path):
@@ -73,7 +76,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 201
+    assert q.abi_version() == 202
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -191,3 +194,24 @@ def test_reorder_rejects_bad_arguments_before_launching(lib):
     assert call(c=cache(b=8, dh=96)) == EDHEAD
     assert call(c=cache(b=8, k=FAKE_MIS)) == EALIGN
     assert call(c=cache(b=0)) == OK                     # nothing to do, nothing launched
+
+
+def test_attend_rejects_bad_arguments_before_launching(lib):
+    a = lib.mqa_attend
+
+    def call(Q=FAKE, K=FAKE, V=FAKE, b=2, n=3, m=5, h=4, G=1, dh=128, dtype=1, mask=None,
+             sb=0, sh=0, sn=0, O=FAKE):
+        return a(Q, K, V, b, n, m, h, G, dh, dtype, 1.0, mask, sb, sh, sn, O, None)
+
+    assert call(Q=None) == ENULL
+    assert call(O=None) == ENULL
+    assert call(n=0) == ESHAPE
+    assert call(m=0) == ESHAPE
+    assert call(h=3, G=2) == ESHAPE
+    assert call(h=64) == ESHAPE                         # h/G > 32
+    assert call(dh=96) == EDHEAD
+    assert call(dtype=3) == EDTYPE
+    assert call(mask=FAKE, sb=-1) == ESHAPE
+    assert call(K=FAKE_MIS) == EALIGN
+    assert call(mask=ctypes.c_void_p(0x7F0000001002)) == EALIGN
+    assert call(b=0) == OK                              # nothing to do, nothing launched
