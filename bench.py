@@ -266,6 +266,39 @@ def prefill_result(cfg, steps, torch, mqa, R=2):
                 causal_flops=flops)
 
 
+def attend_result(cfg, steps, torch, mqa, R=2):
+    """Attention over a fixed memory with a key-padding mask (encoder-decoder
+    attention).  Flops count every (query, memory position) pair: masked
+    logits are computed too."""
+    dev = torch.device("cuda")
+    copies = []
+    for r in range(R):
+        g = torch.Generator(device=dev).manual_seed(cfg.seed * 1000 + r)
+        gc = torch.Generator().manual_seed(cfg.seed * 1000 + r)
+        Q = torch.randn(cfg.b, cfg.n, cfg.h, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        K = torch.randn(cfg.b, cfg.m, cfg.G, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        V = torch.randn(cfg.b, cfg.m, cfg.G, cfg.dh, generator=g, device=dev).to(cfg.dtype)
+        mem = torch.randint(cfg.mem_lo, cfg.mem_hi + 1, (cfg.b,), generator=gc)
+        mask = torch.where(torch.arange(cfg.m)[None, :] < mem[:, None], 0.0, float("-inf"))
+        copies.append((Q, K, V, mask.view(cfg.b, 1, 1, cfg.m).to(dev)))
+    O = torch.empty_like(copies[0][0])
+    for i in range(3):
+        Q, K, V, mk = copies[i % R]
+        mqa.attend(Q, K, V, cfg.scale, mask=mk, out=O)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        Q, K, V, mk = copies[i % R]
+        mqa.attend(Q, K, V, cfg.scale, mask=mk, out=O)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 4 * cfg.b * cfg.h * cfg.dh * cfg.n * cfg.m
+    return dict(ms_per_call=dt * 1e3, tflops=flops / dt / 1e12,
+                mfma_frac_of_peak=flops / dt / 1e12 / BF16_PEAK_TFLOPS, flops=flops)
+
+
 # --------------------------------------------------------------------------- beam
 
 
@@ -468,6 +501,11 @@ def main():
         log("c5 causal prefill")
         extra["c5_prefill_b4_n4096"] = {k: round(v, 4) if isinstance(v, float) else v
                                         for k, v in prefill_result(W.C5, 10, torch, mqa).items()}
+        torch.cuda.empty_cache()
+        log("encoder-decoder attention: non-causal over a fixed memory, key-padding mask")
+        extra["encdec_b4_n4096_m4096"] = {k: round(v, 4) if isinstance(v, float) else v
+                                          for k, v in attend_result(W.ENCDEC, 10, torch,
+                                                                    mqa).items()}
         torch.cuda.empty_cache()
         log("beam-4 step: reorder + fused append + decode, 16 sources x 4 beams")
         extra["beam4_b16x4_ragged8k"] = {k: round(v, 4) if isinstance(v, float) else v
