@@ -85,40 +85,35 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   const bool v_wave = wave < ND;
   const int kw = wave - ND;
-  u32x4 ldv[VPW], ldk[KPW];
-
-  auto issue = [&](int tile) {
+  // One set of in-flight tile chunks: V chunks for the transposing waves,
+  // K chunks for the others (a wave is one or the other).
+  constexpr int KV = KPW > VPW ? KPW : VPW;
+  struct Chunks {
+    u32x4 x[KV];
+  };
+  auto issue = [&](int tile, Chunks& ld) {
     const int pos = tile * kTileRows + col;
     const bool valid = pos < a.m;
-    if (v_wave) {
-      const char* p = vseq + (size_t)pos * rs;
+    const char* p = (v_wave ? vseq : kseq) + (size_t)pos * rs;
 #pragma unroll
-      for (int i = 0; i < VPW; ++i) {
-        const int c = wave * VPW + i;
-        ldv[i] = u32x4{0u, 0u, 0u, 0u};
-        if (valid) ldv[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
-      }
-    } else {
-      const char* p = kseq + (size_t)pos * rs;
-#pragma unroll
-      for (int i = 0; i < KPW; ++i) {
-        const int c = kw + i * NKW;
-        ldk[i] = u32x4{0u, 0u, 0u, 0u};
-        if (c < NQ && valid) ldk[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
-      }
+    for (int i = 0; i < KV; ++i) {
+      const int c = v_wave ? wave * VPW + i : kw + i * NKW;
+      const bool use = v_wave ? (i < VPW) : (c < NQ);
+      ld.x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (use && valid) ld.x[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, const Chunks& ld) {
     if (v_wave) {
       u32x4 ops[VTC];
-      transpose_block<T, VPW>(ldv, 0, sel, ops);
+      transpose_block<T, VPW>(reinterpret_cast<const u32x4(&)[VPW]>(ld.x), 0, sel, ops);
 #pragma unroll
       for (int k = 0; k < VTC; ++k) s_vt[buf][wave][k][lane] = ops[k];
     } else {
 #pragma unroll
       for (int i = 0; i < KPW; ++i) {
         const int c = kw + i * NKW;
-        if (c < NQ) s_k[buf][c][lane] = ldk[i];
+        if (c < NQ) s_k[buf][c][lane] = ld.x[i];
       }
     }
   };
@@ -131,48 +126,59 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   WaveState<ND> st;
   st.reset();
-  issue(0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    commit(buf);
-    __syncthreads();
-    if (it + 1 < ntiles) issue(it + 1);
-    if (it < w_tiles) {
-      u32x4 kr[NQ];
+  auto compute = [&](int it, int buf) {
+    u32x4 kr[NQ];
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
-      const f32x16 s = tile_scores<T, NQ>(kr, qr);
-      const int pos0 = it * kTileRows;
-      float p[16];
-      if constexpr (CAUSAL) {
-        if (pos0 + kTileRows - 1 <= w_row0)
-          softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
-        else
-          softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
-      } else if (a.mask) {
-        float bias[16];
+    for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
+    const f32x16 s = tile_scores<T, NQ>(kr, qr);
+    const int pos0 = it * kTileRows;
+    float p[16];
+    if constexpr (CAUSAL) {
+      if (pos0 + kTileRows - 1 <= w_row0)
+        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
+      else
+        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
+    } else if (a.mask) {
+      float bias[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = pos0 + d_row(r, half);
-          bias[r] = (mrow && j < a.m) ? mrow[j] * kLog2e : 0.f;
-        }
-        softmax_tile<T, ND, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
-      } else {
-        if (pos0 + kTileRows <= a.m)
-          softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
-        else
-          softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+      for (int r = 0; r < 16; ++r) {
+        const int j = pos0 + d_row(r, half);
+        bias[r] = (mrow && j < a.m) ? mrow[j] * kLog2e : 0.f;
       }
-      PvOps<T> pv;
-      pv.set(p);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        u32x4 ops[VTC];
-#pragma unroll
-        for (int k = 0; k < VTC; ++k) ops[k] = s_vt[buf][d][k][lane];
-        st.o[d] = pv.apply(ops, st.o[d]);
-      }
+      softmax_tile<T, ND, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
+    } else {
+      if (pos0 + kTileRows <= a.m)
+        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+      else
+        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
     }
+    PvOps<T> pv;
+    pv.set(p);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      u32x4 ops[VTC];
+#pragma unroll
+      for (int k = 0; k < VTC; ++k) ops[k] = s_vt[buf][d][k][lane];
+      st.o[d] = pv.apply(ops, st.o[d]);
+    }
+  };
+
+  // Tile it is committed to LDS buffer it & 1 from the chunk set it was
+  // loaded into two steps earlier; right after the barrier that set is
+  // refilled with tile it + 2, so loads have two tiles of compute to land.
+  Chunks la, lb;
+  issue(0, la);
+  if (ntiles > 1) issue(1, lb);
+  auto step = [&](int it, Chunks& ld) {
+    const int buf = it & 1;
+    commit(buf, ld);
+    __syncthreads();
+    if (it + 2 < ntiles) issue(it + 2, ld);
+    if (it < w_tiles) compute(it, buf);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, la);
+    if (it + 1 < ntiles) step(it + 1, lb);
   }
 
   const float l_tot = st.l + xor32(st.l);
