@@ -200,10 +200,18 @@ template <> struct PvOps<float> {
 
 // Online-softmax step: scale the raw scores, add the additive mask `bias`
 // (already in log2 units) when BIAS, mask positions beyond this lane's limit
-// (pos > lim) unless FULL, update (m, l), rescale o, and return the
-// unnormalised probabilities p (exp2 of logit minus the new max).  For bf16
-// the probabilities are rounded to bf16 before they are summed, so the
+// (pos > lim) unless FULL, update (m, l), rescale o when needed, and return
+// the unnormalised probabilities p = exp2(logit - m).  For bf16 the
+// probabilities are rounded to bf16 before they are summed, so the
 // normaliser l is the sum of exactly the weights the PV product uses.
+//
+// The reference m may lag the true running max: it is raised (and o, l
+// rescaled) only when some column's tile max exceeds it by more than
+// kRescaleSlack, so after the first tile the rescale is rare.  p is then at
+// most 2^kRescaleSlack, far inside fp32 range, and o and l always share the
+// same reference, so o / l is unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
 template <typename T, int ND, bool FULL, bool BIAS = false>
 __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s, float scale_log2,
                                              int pos0, int lim, int half, float (&p)[16],
@@ -219,10 +227,19 @@ __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s,
 #pragma unroll
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, t[r]);
   mt = fmaxf(mt, xor32(mt));
-  const float m_new = fmaxf(st.m, mt);
-  // A column with no visible position yet keeps m = -inf; use 0 as the
-  // reference so exp2 sees -inf - 0 (= 0) and never -inf - (-inf).
-  const float ref = (m_new == kNegInf) ? 0.f : m_new;
+  // st.m == -inf (nothing visible yet) compares as -inf + slack = -inf, so
+  // the first visible position always raises it.
+  if (__any(mt > st.m + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m, mt);
+    // A column with no visible position yet keeps m = -inf; use 0 as the
+    // reference so exp2 sees -inf - 0 (= 0) and never -inf - (-inf).
+    const float alpha = fast_exp2(st.m - (m_new == kNegInf ? 0.f : m_new));
+#pragma unroll
+    for (int d = 0; d < ND; ++d) st.o[d] *= alpha;
+    st.l *= alpha;
+    st.m = m_new;
+  }
+  const float ref = (st.m == kNegInf) ? 0.f : st.m;
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -230,14 +247,7 @@ __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s,
     if constexpr (sizeof(T) == 2) p[r] = (float)(__bf16)p[r];
     psum += p[r];
   }
-  if (__any(m_new != st.m)) {
-    const float alpha = fast_exp2(st.m - ref);
-#pragma unroll
-    for (int d = 0; d < ND; ++d) st.o[d] *= alpha;
-    st.l *= alpha;
-  }
   st.l += psum;
-  st.m = m_new;
 }
 
 }  // namespace mqa

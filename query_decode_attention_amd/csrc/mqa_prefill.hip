@@ -40,9 +40,8 @@ template <typename T, int DH, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
-  static_assert(NW > ND, "needs waves beyond the V transposers");
-  constexpr int NKW = NW - ND;                // waves staging K chunks
-  constexpr int KPW = (NQ + NKW - 1) / NKW;   // K chunks per K wave
+  static_assert(NW >= ND, "a wave per d block transposes V");
+  constexpr int KPW = (NQ + NW - 1) / NW;     // K chunks per wave
   constexpr int VPW = NQ / ND;                // V chunks per d block
   __shared__ u32x4 s_k[2][NQ][64];
   __shared__ u32x4 s_vt[2][ND][VTC][64];
@@ -83,38 +82,44 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const char* kseq = a.K + seq_off;
   const char* vseq = a.V + seq_off;
 
+  // Every wave stages K chunks wave, wave + NW, ...; waves below ND also
+  // transpose d block `wave` of V into the PV operand layout.
   const bool v_wave = wave < ND;
-  const int kw = wave - ND;
-  // One set of in-flight tile chunks: V chunks for the transposing waves,
-  // K chunks for the others (a wave is one or the other).
-  constexpr int KV = KPW > VPW ? KPW : VPW;
   struct Chunks {
-    u32x4 x[KV];
+    u32x4 k[KPW];
+    u32x4 v[VPW];
   };
   auto issue = [&](int tile, Chunks& ld) {
     const int pos = tile * kTileRows + col;
     const bool valid = pos < a.m;
-    const char* p = (v_wave ? vseq : kseq) + (size_t)pos * rs;
+    const char* kp = kseq + (size_t)pos * rs;
+    const char* vp = vseq + (size_t)pos * rs;
 #pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int c = v_wave ? wave * VPW + i : kw + i * NKW;
-      const bool use = v_wave ? (i < VPW) : (c < NQ);
-      ld.x[i] = u32x4{0u, 0u, 0u, 0u};
-      if (use && valid) ld.x[i] = *reinterpret_cast<const u32x4*>(p + (2 * c + half) * 16);
+    for (int i = 0; i < KPW; ++i) {
+      const int c = wave + i * NW;
+      ld.k[i] = u32x4{0u, 0u, 0u, 0u};
+      if (c < NQ && valid) ld.k[i] = *reinterpret_cast<const u32x4*>(kp + (2 * c + half) * 16);
+    }
+    if (v_wave) {
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) {
+        const int c = wave * VPW + i;
+        ld.v[i] = u32x4{0u, 0u, 0u, 0u};
+        if (valid) ld.v[i] = *reinterpret_cast<const u32x4*>(vp + (2 * c + half) * 16);
+      }
     }
   };
   auto commit = [&](int buf, const Chunks& ld) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int c = wave + i * NW;
+      if (c < NQ) s_k[buf][c][lane] = ld.k[i];
+    }
     if (v_wave) {
       u32x4 ops[VTC];
-      transpose_block<T, VPW>(reinterpret_cast<const u32x4(&)[VPW]>(ld.x), 0, sel, ops);
+      transpose_block<T, VPW>(ld.v, 0, sel, ops);
 #pragma unroll
       for (int k = 0; k < VTC; ++k) s_vt[buf][wave][k][lane] = ops[k];
-    } else {
-#pragma unroll
-      for (int i = 0; i < KPW; ++i) {
-        const int c = kw + i * NKW;
-        if (c < NQ) s_k[buf][c][lane] = ld.x[i];
-      }
     }
   };
 
