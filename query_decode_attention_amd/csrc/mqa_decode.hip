@@ -11,9 +11,11 @@
 //                      of a fused append.
 //
 // Work decomposition.  The visible positions of every (sequence b, group g)
-// are cut into tiles of 32.  All tiles of all segments form one flat list of
-// T tiles; workgroup w of a grid of W takes tiles [T*w/W, T*(w+1)/W), so every
-// workgroup streams the same number of bytes whatever the length mix.  Each
+// segment are cut into tiles of 32.  All segments form one flat list of U
+// units -- kSegLead lead-in units, then the segment's tiles -- and workgroup
+// w of a grid of W takes units [U*w/W, U*(w+1)/W): every workgroup streams
+// about the same number of bytes whatever the length mix, a few tiles fewer
+// for each segment boundary its range crosses (see kSegLead).  Each
 // wave derives this schedule from lens by itself (wave-wide scan) and keeps
 // the lens entries it needs in registers, so the schedule costs no host
 // synchronisation, no barrier and one read of lens.
@@ -127,19 +129,30 @@ __device__ __forceinline__ int tiles_of(const SeqView& s) {
   return (s.L - s.j0 + kTileRows - 1) / kTileRows;
 }
 
-// Workgroups that share the T tiles of `segs` non-empty segments: the
-// launched grid, but no more than one per `min_tiles` tiles unless there are
+// Schedule units.  Every non-empty segment is kSegLead virtual units (no
+// positions) followed by its tiles, and workgroups split the units evenly.  A
+// workgroup whose range reaches into a further segment thereby takes about
+// kSegLead fewer tiles, which pays for the fold at the segment boundary (the
+// waves of a workgroup meet there, so its critical path grows by about half
+// a round of tiles per boundary crossed).
+constexpr int kSegLead = 6;
+
+// Workgroups that share the Tv units of `segs` non-empty segments: the
+// launched grid, but no more than one per `min_tiles` units unless there are
 // more segments than that (short segments are better run side by side than
-// one after another).  Both kernels derive the same value.
-__device__ __forceinline__ int effective_grid(int64_t T, int64_t segs, int grid, int min_tiles) {
-  int64_t w = (T + min_tiles - 1) / min_tiles;
+// one after another), and no more than Tv / (kSegLead + 1), so that every
+// range of units holds at least one tile.  Both kernels derive the same value.
+__device__ __forceinline__ int effective_grid(int64_t Tv, int64_t segs, int grid, int min_tiles) {
+  int64_t w = (Tv + min_tiles - 1) / min_tiles;
   if (w < segs) w = segs;
-  return (int)(w < 1 ? 1 : (w < grid ? w : grid));
+  if (w > grid) w = grid;
+  if (w > Tv / (kSegLead + 1)) w = Tv / (kSegLead + 1);
+  return (int)(w < 1 ? 1 : w);
 }
 
-// First flat tile of workgroup w out of W over T tiles.
+// First unit of workgroup w out of W over T units.
 __device__ __forceinline__ int64_t wg_start(int64_t T, int w, int W) { return T * w / W; }
-// Workgroup whose range contains flat tile t (T > 0).
+// Workgroup whose range contains unit t (T > 0).
 __device__ __forceinline__ int wg_of(int64_t t, int64_t T, int W) {
   return (int)(((t + 1) * W + T - 1) / T) - 1;
 }
@@ -301,6 +314,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int row = lane & 31, half = lane >> 5;
 
   // ---- schedule (each wave on its own) ----
+  // Units of sequence b per group: tiles + kSegLead, or 0 when empty.
   // raw0: lens entry of sequence `lane` (the first 64), reused below.
   int total = 0, nonempty = 0, raw0 = 0;
   for (int c = 0; c < a.b; c += 64) {
@@ -308,6 +322,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (c + lane < a.b) {
       raw = a.lens[c + lane];
       v = tiles_of(seq_view_raw(a, raw));
+      v = v > 0 ? v + kSegLead : 0;
     }
     if (c == 0) raw0 = raw;
     const int incl = wave_incl_scan(v, lane);
@@ -320,10 +335,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     a.prefix[a.b + 1] = nonempty;
   }
   total = __builtin_amdgcn_readfirstlane(total);
-  const int64_t Tt = (int64_t)total * a.G;
+  nonempty = __builtin_amdgcn_readfirstlane(nonempty);
+  const int64_t Tt = (int64_t)total * a.G;                  // units
+  const int64_t segs = (int64_t)nonempty * a.G;
   // Workgroups in use (see effective_grid): every wave has work, short
   // segments still run side by side.
-  const int W = effective_grid(Tt, (int64_t)nonempty * a.G, gridDim.x, NW);
+  const int W = effective_grid(Tt, segs, gridDim.x, NW);
   const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
 
   // lens entries of sequences cbase .. cbase + 63, one per lane: the segment
@@ -337,6 +354,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       int raw = raw0, v = 0;
       if (c > 0) raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
       if (c + lane < a.b) v = tiles_of(seq_view_raw(a, raw));
+      v = v > 0 ? v + kSegLead : 0;
       const int incl = wave_incl_scan(v, lane);
       const int64_t lo = (int64_t)(run + incl - v) * a.G, hi = (int64_t)(run + incl) * a.G;
       const uint64_t hit = __ballot(c + lane < a.b && v > 0 && lo <= t0 && t0 < hi);
@@ -391,6 +409,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       } while (bn < a.b && tiles_of(seq_view_raw(a, raw_of(bn))) == 0);
     }
   };
+  int done = 0;           // tiles of this workgroup's range taken so far
   int qb = 0;             // Q^T buffer of the current segment
   bool q_staged = false;  // ... already copied during the previous segment
   bool first = true;
@@ -405,18 +424,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       ++b_cur;
       continue;
     }
-    const int g = (int)((t - seg_base) / nb);
-    const int64_t seg0 = seg_base + (int64_t)g * nb;
-    const int ta = (int)(t - seg0);
+    const int unit = nb + kSegLead;  // units of one group of this sequence
+    const int g = (int)((t - seg_base) / unit);
+    const int64_t seg0 = seg_base + (int64_t)g * unit + kSegLead;  // its first tile
+    const int ta = (int)((t > seg0 ? t : seg0) - seg0);
     const int te = (int)((t1 < seg0 + nb ? t1 : seg0 + nb) - seg0);
+    if (te <= ta) break;  // the range ends inside this segment's lead-in units
     const bool complete = (ta == 0 && te == nb);
-    const bool last_seg = (seg0 + te >= t1);
+    // the range goes on into the next segment's tiles
+    const bool last_seg = !(te == nb && seg0 + nb + kSegLead < t1);
 
     // ---- this wave's tiles ----
     // Tiles go round-robin over the waves by their index in the workgroup's
     // range (not in the segment), so a range that spans segments still gives
     // every wave the same number of tiles, to within one.
-    const int rel0 = (int)(t - t0);  // workgroup-relative index of tile ta
+    const int rel0 = done;  // workgroup-relative index of tile ta
     int tile = ta + ((wave - rel0) % NW + NW) % NW;
     const size_t seq_off = ((size_t)b_cur * a.m_cap * a.G + (size_t)g) * DH * sizeof(T);
     const size_t new_off = ((size_t)b_cur * a.G + (size_t)g) * DH * sizeof(T);
@@ -531,9 +553,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (next_staged) qb ^= 1;
     q_staged = next_staged;
     first = false;
+    done += te - ta;
     t = seg0 + te;
     if (g == a.G - 1 && te == nb) {
-      seg_base += (int64_t)a.G * nb;
+      seg_base += (int64_t)a.G * unit;
       ++b_cur;
     }
   }
@@ -559,11 +582,10 @@ struct CombineArgs {
 // batch costs one memory round trip; there is no LDS and no barrier.
 // Block (seg, y) handles the heads [y*HPB, (y+1)*HPB) of segment seg.
 //
-// Every workgroup of the decode grid has a non-empty tile range (the
-// effective grid never exceeds the tile count T, since each non-empty segment
-// holds at least one tile), so every workgroup in [wf, wl] wrote a record for
-// this segment: slot 1 for wf when its range began in an earlier segment,
-// slot 0 otherwise.
+// Every workgroup in [wf, wl] took tiles of this segment and wrote a record
+// for it (every range of units holds a tile: the effective grid keeps ranges
+// longer than a lead-in): slot 1 for wf when its range began in an earlier
+// segment, slot 0 otherwise.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int kD4 = DH / 4;            // float4 words per head row
@@ -582,14 +604,18 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
   const int seg = blockIdx.x;
   const int bi = seg / a.G, g = seg % a.G;
-  const int nb = a.prefix[bi + 1] - a.prefix[bi];
-  if (nb == 0) return;
+  const int unit = a.prefix[bi + 1] - a.prefix[bi];  // lead-in units + tiles, or 0
+  if (unit == 0) return;
+  const int nb = unit - kSegLead;
   const int64_t Tt = (int64_t)a.prefix[a.b] * a.G;
-  const int W = effective_grid(Tt, (int64_t)a.prefix[a.b + 1] * a.G, a.grid, a.min_tiles);
-  const int64_t S0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * nb;
+  const int64_t segs = (int64_t)a.prefix[a.b + 1] * a.G;
+  const int W = effective_grid(Tt, segs, a.grid, a.min_tiles);
+  const int64_t U0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * unit;  // first unit
+  const int64_t S0 = U0 + kSegLead;                                       // first tile
   const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
-  const int first_slot = (wg_start(Tt, wf, W) < S0) ? 1 : 0;
+  // wf's range began in an earlier segment (whose last tile is unit U0 - 1)
+  const int first_slot = (wg_start(Tt, wf, W) < U0) ? 1 : 0;
 
   const int hl = threadIdx.x / kD4, d4 = threadIdx.x % kD4;
   const int hd = blockIdx.y * HPB + hl;
