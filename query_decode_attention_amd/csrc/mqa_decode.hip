@@ -205,7 +205,7 @@ __device__ __forceinline__ void tile_update(WaveState<TileShape<T, DH>::ND>& st,
 #pragma unroll
   for (int c = 0; c < NQ; ++c) qr[c] = s_q[c][lane];
   const f32x16 s = tile_scores<T, NQ>(kr, qr);
-  float p[16];
+  ProbTile<T> p;
   softmax_tile<T, ND, FULL>(st, s, scale_log2, pos0, L - 1, half, p);
   PvOps<T> pv;
   pv.set(p);

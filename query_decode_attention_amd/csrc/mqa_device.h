@@ -171,14 +171,25 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&vr)[NQ], int blk,
   }
 }
 
+// The P^T operand of one tile: the unnormalised probabilities of this lane's
+// 16 positions (rows d_row(r, half) of the tile), bf16-packed for bf16 inputs.
+template <typename T>
+struct ProbTile;
+template <> struct ProbTile<__bf16> {
+  bf16x8 pb[2];
+};
+template <> struct ProbTile<float> {
+  float pf[16];
+};
+
 // Weighted-V products of one d block: o += V_block^T . P^T.
 template <typename T>
 struct PvOps;
 template <> struct PvOps<__bf16> {
   bf16x8 pb[2];
-  __device__ __forceinline__ void set(const float (&p)[16]) {
-    pb[0] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    pb[1] = pack_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+  __device__ __forceinline__ void set(const ProbTile<__bf16>& pt) {
+    pb[0] = pt.pb[0];
+    pb[1] = pt.pb[1];
   }
   __device__ __forceinline__ f32x16 apply(const u32x4 (&ops)[2], f32x16 o) const {
     o = mfma_bf16(as_bf16x8(ops[0]), pb[0], o);
@@ -187,9 +198,9 @@ template <> struct PvOps<__bf16> {
 };
 template <> struct PvOps<float> {
   float pf[16];
-  __device__ __forceinline__ void set(const float (&p)[16]) {
+  __device__ __forceinline__ void set(const ProbTile<float>& pt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pf[r] = p[r];
+    for (int r = 0; r < 16; ++r) pf[r] = pt.pf[r];
   }
   __device__ __forceinline__ f32x16 apply(const u32x4 (&ops)[4], f32x16 o) const {
 #pragma unroll
@@ -201,9 +212,12 @@ template <> struct PvOps<float> {
 // Online-softmax step: scale the raw scores, add the additive mask `bias`
 // (already in log2 units) when BIAS, mask positions beyond this lane's limit
 // (pos > lim) unless FULL, update (m, l), rescale o when needed, and return
-// the unnormalised probabilities p = exp2(logit - m).  For bf16 the
-// probabilities are rounded to bf16 before they are summed, so the
-// normaliser l is the sum of exactly the weights the PV product uses.
+// the unnormalised probabilities p = exp2(logit - m) as the PV operand.  For
+// bf16 the probabilities are rounded to bf16 and the normaliser l sums
+// exactly the rounded values the PV product uses.
+//
+// FOLD (requires scale_log2 > 0 and no bias): the max is taken over the raw
+// scores and scaled once, and each probability is exp2(fma(s, scale, -m)).
 //
 // The reference m may lag the true running max: it is raised (and o, l
 // rescaled) only when some column's tile max exceeds it by more than
@@ -212,21 +226,23 @@ template <> struct PvOps<float> {
 // same reference, so o / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int ND, bool FULL, bool BIAS = false>
+template <typename T, int ND, bool FULL, bool BIAS = false, bool FOLD = false>
 __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s, float scale_log2,
-                                             int pos0, int lim, int half, float (&p)[16],
+                                             int pos0, int lim, int half, ProbTile<T>& pt,
                                              const float* bias = nullptr) {
-  float t[16];
+  static_assert(!(FOLD && BIAS), "the folded form has no bias");
+  float x[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    t[r] = s[r] * scale_log2;
-    if constexpr (BIAS) t[r] += bias[r];
-    if (!FULL && pos0 + d_row(r, half) > lim) t[r] = kNegInf;
+    x[r] = FOLD ? s[r] : s[r] * scale_log2;
+    if constexpr (BIAS) x[r] += bias[r];
+    if (!FULL && pos0 + d_row(r, half) > lim) x[r] = kNegInf;
   }
-  float mt = t[0];
+  float mt = x[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, t[r]);
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
   mt = fmaxf(mt, xor32(mt));
+  if constexpr (FOLD) mt *= scale_log2;  // -inf stays -inf (scale_log2 > 0)
   // st.m == -inf (nothing visible yet) compares as -inf + slack = -inf, so
   // the first visible position always raises it.
   if (__any(mt > st.m + kRescaleSlack)) {
@@ -240,12 +256,28 @@ __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s,
     st.m = m_new;
   }
   const float ref = (st.m == kNegInf) ? 0.f : st.m;
-  float psum = 0.f;
+  float e[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    p[r] = fast_exp2(t[r] - ref);
-    if constexpr (sizeof(T) == 2) p[r] = (float)(__bf16)p[r];
-    psum += p[r];
+  for (int r = 0; r < 16; ++r)
+    e[r] = fast_exp2(FOLD ? __builtin_fmaf(x[r], scale_log2, -ref) : x[r] - ref);
+  float psum = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    pt.pb[0] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    pt.pb[1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    // the rounded values, widened back exactly (bf16 is the top half of fp32)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 w = __builtin_bit_cast(u32x4, pt.pb[k]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        psum += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pt.pf[r] = e[r];
+      psum += e[r];
+    }
   }
   st.l += psum;
 }

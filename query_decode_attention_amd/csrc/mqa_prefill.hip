@@ -36,7 +36,9 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-template <typename T, int DH, int NW, bool CAUSAL>
+// FOLD: the softmax takes its max over the raw scores and folds the scale
+// into one FMA per score (only for scale > 0; chosen at launch).
+template <typename T, int DH, int NW, bool CAUSAL, bool FOLD>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
@@ -137,13 +139,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
     const f32x16 s = tile_scores<T, NQ>(kr, qr);
     const int pos0 = it * kTileRows;
-    float p[16];
+    ProbTile<T> p;
     if constexpr (CAUSAL) {
       if (pos0 + kTileRows - 1 <= w_row0)
-        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, crow, half, p);
+        softmax_tile<T, ND, true, false, FOLD>(st, s, a.scale_log2, pos0, crow, half, p);
       else
-        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, crow, half, p);
-    } else if (a.mask) {
+        softmax_tile<T, ND, false, false, FOLD>(st, s, a.scale_log2, pos0, crow, half, p);
+    } else if (!FOLD && a.mask) {  // masked runs use the unfolded form
       float bias[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -153,9 +155,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       softmax_tile<T, ND, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
     } else {
       if (pos0 + kTileRows <= a.m)
-        softmax_tile<T, ND, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+        softmax_tile<T, ND, true, false, FOLD>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
       else
-        softmax_tile<T, ND, false>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+        softmax_tile<T, ND, false, false, FOLD>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
     }
     PvOps<T> pv;
     pv.set(p);
@@ -264,8 +266,12 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   }
   const PrefillArgs a = row_blocks(p, p.n);
   const size_t blocks = (size_t)p.b * p.G * a.nrb;
-  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true>), dim3((unsigned)blocks),
-                     dim3(kPrefillWaves * 64), 0, s, a);
+  if (a.scale_log2 > 0.f)
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, true>), dim3((unsigned)blocks),
+                       dim3(kPrefillWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, false>),
+                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -277,8 +283,12 @@ hipError_t launch_attend_t(const AttendParams& q, hipStream_t s) {
   a.msh = q.msh;
   a.msn = q.msn;
   const size_t blocks = (size_t)q.base.b * q.base.G * a.nrb;
-  hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false>), dim3((unsigned)blocks),
-                     dim3(kPrefillWaves * 64), 0, s, a);
+  if (a.scale_log2 > 0.f && !a.mask)
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, true>),
+                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false>),
+                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace
