@@ -37,6 +37,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Combine a value with the one held by lane ^ 32, through one cross-half
+// swap (v_permlane32_swap: each lane receives the values of lanes l % 32 and
+// l % 32 + 32, in that order, so both halves compute the same result).
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- bf16 <-> u32x4 bit casts -------------------------------------------------
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -226,7 +240,10 @@ template <> struct PvOps<float> {
 // same reference, so o / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int ND, bool FULL, bool BIAS = false, bool FOLD = false>
+// SWAP: the cross-half max uses v_permlane32_swap instead of an LDS
+// permute (faster in the compute-bound prefill; the memory-bound decode
+// measured slower with it at long context, so it keeps the permute).
+template <typename T, int ND, bool FULL, bool BIAS = false, bool FOLD = false, bool SWAP = false>
 __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s, float scale_log2,
                                              int pos0, int lim, int half, ProbTile<T>& pt,
                                              const float* bias = nullptr) {
@@ -241,7 +258,7 @@ __device__ __forceinline__ void softmax_tile(WaveState<ND>& st, const f32x16& s,
   float mt = x[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-  mt = fmaxf(mt, xor32(mt));
+  mt = SWAP ? max_halves(mt) : fmaxf(mt, xor32(mt));
   if constexpr (FOLD) mt *= scale_log2;  // -inf stays -inf (scale_log2 > 0)
   // st.m == -inf (nothing visible yet) compares as -inf + slack = -inf, so
   // the first visible position always raises it.

@@ -142,9 +142,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     ProbTile<T> p;
     if constexpr (CAUSAL) {
       if (pos0 + kTileRows - 1 <= w_row0)
-        softmax_tile<T, ND, true, false, FOLD>(st, s, a.scale_log2, pos0, crow, half, p);
+        softmax_tile<T, ND, true, false, FOLD, true>(st, s, a.scale_log2, pos0, crow, half, p);
       else
-        softmax_tile<T, ND, false, false, FOLD>(st, s, a.scale_log2, pos0, crow, half, p);
+        softmax_tile<T, ND, false, false, FOLD, true>(st, s, a.scale_log2, pos0, crow, half, p);
     } else if (!FOLD && a.mask) {  // masked runs use the unfolded form
       float bias[16];
 #pragma unroll
@@ -152,12 +152,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         const int j = pos0 + d_row(r, half);
         bias[r] = (mrow && j < a.m) ? mrow[j] * kLog2e : 0.f;
       }
-      softmax_tile<T, ND, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
+      softmax_tile<T, ND, false, true, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
     } else {
       if (pos0 + kTileRows <= a.m)
-        softmax_tile<T, ND, true, false, FOLD>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+        softmax_tile<T, ND, true, false, FOLD, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
       else
-        softmax_tile<T, ND, false, false, FOLD>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
+        softmax_tile<T, ND, false, false, FOLD, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p);
     }
     PvOps<T> pv;
     pv.set(p);
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     if (it + 1 < ntiles) step(it + 1, lb);
   }
 
-  const float l_tot = st.l + xor32(st.l);
+  const float l_tot = sum_halves(st.l);
   if (col_ok) {
     // a row whose every key is masked out gets zeros (as an empty decode row)
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
