@@ -37,8 +37,11 @@ struct PrefillArgs {
 };
 
 // FOLD: the softmax takes its max over the raw scores and folds the scale
-// into one FMA per score (only for scale > 0; chosen at launch).
-template <typename T, int DH, int NW, bool CAUSAL, bool FOLD>
+// into one FMA per score (only for scale > 0 and no mask; chosen at launch).
+// MASK (non-causal only): kMaskNone, kMaskKeys (one value per key: the
+// head and query strides are 0, as for key padding) or kMaskFull.
+constexpr int kMaskNone = 0, kMaskKeys = 1, kMaskFull = 2;
+template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int VPW = NQ / ND;                // V chunks per d block
   __shared__ u32x4 s_k[2][NQ][64];
   __shared__ u32x4 s_vt[2][ND][VTC][64];
+  __shared__ f32x4 s_kb[2][kTileRows / 4];  // per-key mask of the tile (key padding)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -87,9 +91,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // Every wave stages K chunks wave, wave + NW, ...; waves below ND also
   // transpose d block `wave` of V into the PV operand layout.
   const bool v_wave = wave < ND;
+  // A key-padding mask (one value per key) travels with the tile: the last
+  // wave loads the tile's 32 values with its chunks and stages them in LDS.
+  const bool kb_wave = MASK == kMaskKeys && wave == NW - 1;
+  const float* kb_row = kb_wave ? a.mask + (int64_t)bi * a.msb : nullptr;
   struct Chunks {
     u32x4 k[KPW];
     u32x4 v[VPW];
+    float kb;
   };
   auto issue = [&](int tile, Chunks& ld) {
     const int pos = tile * kTileRows + col;
@@ -110,6 +119,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         if (valid) ld.v[i] = *reinterpret_cast<const u32x4*>(vp + (2 * c + half) * 16);
       }
     }
+    if (kb_wave) ld.kb = valid ? kb_row[pos] * 1.4426950408889634f : 0.f;  // log2 units
   };
   auto commit = [&](int buf, const Chunks& ld) {
 #pragma unroll
@@ -123,17 +133,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int k = 0; k < VTC; ++k) s_vt[buf][wave][k][lane] = ops[k];
     }
+    if (kb_wave && half == 0) reinterpret_cast<float*>(s_kb[buf])[col] = ld.kb;
   };
 
   // additive mask row of this lane's column (non-causal only)
   const float* mrow = nullptr;
-  if (!CAUSAL && a.mask && col_ok)
+  if (MASK == kMaskFull && col_ok)
     mrow = a.mask + (int64_t)bi * a.msb + (int64_t)(g * a.hg + chead) * a.msh + (int64_t)crow * a.msn;
   constexpr float kLog2e = 1.4426950408889634f;
 
   WaveState<ND> st;
   st.reset();
   auto compute = [&](int it, int buf) {
+    // a general mask's values are fetched before the score product so that
+    // its latency overlaps the MFMAs
+    float mk[16];
+    if constexpr (MASK == kMaskFull) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = it * kTileRows + d_row(r, half);
+        mk[r] = (mrow && j < a.m) ? mrow[j] : 0.f;
+      }
+    }
     u32x4 kr[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
@@ -145,12 +166,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         softmax_tile<T, ND, true, false, FOLD, true>(st, s, a.scale_log2, pos0, crow, half, p);
       else
         softmax_tile<T, ND, false, false, FOLD, true>(st, s, a.scale_log2, pos0, crow, half, p);
-    } else if (!FOLD && a.mask) {  // masked runs use the unfolded form
+    } else if constexpr (MASK != kMaskNone) {
       float bias[16];
+      if constexpr (MASK == kMaskKeys) {
+        // keys 8k + 4*half .. +3 of the tile for registers 4k .. 4k+3
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = pos0 + d_row(r, half);
-        bias[r] = (mrow && j < a.m) ? mrow[j] * kLog2e : 0.f;
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 kb = s_kb[buf][2 * k + half];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bias[r] = mk[r] * kLog2e;
       }
       softmax_tile<T, ND, false, true, false, true>(st, s, a.scale_log2, pos0, a.m - 1, half, p, bias);
     } else {
@@ -267,10 +295,10 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   const PrefillArgs a = row_blocks(p, p.n);
   const size_t blocks = (size_t)p.b * p.G * a.nrb;
   if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, true>), dim3((unsigned)blocks),
-                       dim3(kPrefillWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, true, kMaskNone>),
+                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, false>),
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, false, kMaskNone>),
                        dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -283,12 +311,19 @@ hipError_t launch_attend_t(const AttendParams& q, hipStream_t s) {
   a.msh = q.msh;
   a.msn = q.msn;
   const size_t blocks = (size_t)q.base.b * q.base.G * a.nrb;
-  if (a.scale_log2 > 0.f && !a.mask)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, true>),
-                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(kPrefillWaves * 64);
+  if (q.mask && q.msh == 0 && q.msn == 0)
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskKeys>), grid,
+                       block, 0, s, a);
+  else if (q.mask)
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskFull>), grid,
+                       block, 0, s, a);
+  else if (a.scale_log2 > 0.f)
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, true, kMaskNone>), grid,
+                       block, 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false>),
-                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskNone>), grid,
+                       block, 0, s, a);
   return hipGetLastError();
 }
 }  // namespace
