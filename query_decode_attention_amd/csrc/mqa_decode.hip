@@ -295,6 +295,19 @@ __device__ __forceinline__ void copy_q(const DecodeArgs& a, u32x4 (*s_q)[64], in
   for (int c = wave; c < NQ; c += NW) load_to_lds(qp + (2 * c + half) * 16, &s_q[c][0]);
 }
 
+// The whole Q^T operand copied by one wave into an LDS region of its own
+// (no other wave reads it, so no barrier is needed); complete once this
+// wave's vmcnt reaches 0.
+template <typename T, int DH>
+__device__ __forceinline__ void copy_q_own(const DecodeArgs& a, u32x4 (*dst)[64], int bi, int g,
+                                           int lane) {
+  constexpr int NQ = TileShape<T, DH>::NQ;
+  const int half = lane >> 5;
+  const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) load_to_lds(qp + (2 * c + half) * 16, &dst[c][0]);
+}
+
 // ------------------------------------------------------------ decode: kernel ----
 
 template <typename T, int DH, int NW>
@@ -309,9 +322,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   __shared__ WaveSlot<ND> s_slot[NW];
   __shared__ u32x4 s_q[kQBufs][NQ][64];  // Q^T operand(s)
   __shared__ float s_fold[2][32];        // per-head max and sum of the folded state
+  // In the first segment a wave reads Q^T from its own fold slot, which it
+  // does not need before it parks.
+  static_assert(NQ * 64 * sizeof(u32x4) <= sizeof(WaveSlot<ND>), "Q^T fits a fold slot");
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
   const int row = lane & 31, half = lane >> 5;
+  u32x4 (*const own_q)[64] = reinterpret_cast<u32x4 (*)[64]>(&s_slot[wave]);
 
   // ---- schedule (each wave on its own) ----
   // Units of sequence b per group: tiles + kSegLead, or 0 when empty.
@@ -463,19 +481,34 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(vc + (2 * c + half) * 16) = vr[c];
       }
     };
+    const u32x4 (*qsrc)[64] = s_q[qb];  // Q^T operand of this segment
+    bool own = false;                    // ... in this wave's own slot
     WaveState<ND> st;
     st.reset();
     auto update = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
       const int pos0 = j0 + tl * kTileRows;
       if (pos0 + kTileRows <= L)
-        tile_update<T, DH, true>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, true>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
       else
-        tile_update<T, DH, false>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, false>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
     };
 
     // ---- Q^T of this segment, and the copy of the next one's ----
-    if (!q_staged) stage_q<T, DH, NW>(a, s_q[qb], b_cur, g, wave, lane);
-    __syncthreads();
+    // First segment: every wave with tiles copies the whole operand into its
+    // own fold slot, so no wave waits for another and the copy shares its
+    // round trip with the wave's first tile.  Later segments: the operand was
+    // copied during the previous segment, or (one buffer) all waves stage it
+    // now.
+    if (first) {
+      qsrc = own_q;
+      if (tile < te) {
+        copy_q_own<T, DH>(a, own_q, b_cur, g, lane);
+        own = true;
+      }
+    } else if (!q_staged) {
+      stage_q<T, DH, NW>(a, s_q[qb], b_cur, g, wave, lane);
+      __syncthreads();
+    }
     // When the range goes on, the next segment's Q^T is copied into the
     // other buffer now and lands while this segment streams.
     bool next_staged = false;
@@ -494,7 +527,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       if (pos0 + kTileRows <= L && app_pos < pos0) {
         const size_t off = seq_off + (size_t)(pos0 + row) * row_stride;
         load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
-        tile_update<T, DH, true>(st, kr, vr, s_q[qb], lane, sel, a.scale_log2, pos0, L, half);
+        tile_update<T, DH, true>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
       } else {
         // last tile of the segment: ragged, and/or holding the appended row
         const char *kp, *vp;
@@ -505,8 +538,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
     }
     // This wave's part of the next Q^T has landed before the barriers below,
-    // which publish it.
-    if (next_staged) __builtin_amdgcn_s_waitcnt(0x0F70);
+    // which publish it, and its own copy of Q^T before it parks over it.
+    if (next_staged || own) __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // ---- fold the waves: park in LDS, combine in a fixed order ----
     park<ND>(st, s_slot[wave], lane);
