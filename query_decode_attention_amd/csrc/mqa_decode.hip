@@ -321,7 +321,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       NW * sizeof(WaveSlot<ND>) + 2 * NQ * 64 * sizeof(u32x4) + 256 <= 160 * 1024 ? 2 : 1;
   __shared__ WaveSlot<ND> s_slot[NW];
   __shared__ u32x4 s_q[kQBufs][NQ][64];  // Q^T operand(s)
-  __shared__ float s_fold[2][32];        // per-head max and sum of the folded state
   // In the first segment a wave reads Q^T from its own fold slot, which it
   // does not need before it parks.
   static_assert(NQ * 64 * sizeof(u32x4) <= sizeof(WaveSlot<ND>), "Q^T fits a fold slot");
@@ -521,63 +520,77 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
     }
 
+    // The Q^T copies issued above must land before this wave reads its own
+    // copy, before the barriers below publish the next segment's, and before
+    // the wave parks over its own.  The wait is taken with the first tile,
+    // whose loads it needs anyway, so it never covers the appended row's
+    // stores (waiting on those would hold up the fold).
+    bool dma_wait = next_staged || own;
     for (; tile < te; tile += NW) {
       const int pos0 = j0 + tile * kTileRows;
       u32x4 kr[NQ], vr[NQ];
       if (pos0 + kTileRows <= L && app_pos < pos0) {
         const size_t off = seq_off + (size_t)(pos0 + row) * row_stride;
         load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
+        if (dma_wait) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          dma_wait = false;
+        }
         tile_update<T, DH, true>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
       } else {
         // last tile of the segment: ragged, and/or holding the appended row
         const char *kp, *vp;
         const bool valid = row_ptrs(tile, kp, vp);
         load_kv<NQ, false>(kp, vp, valid, half, kr, vr);
+        if (dma_wait) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          dma_wait = false;
+        }
         store_new_row(tile, kr, vr);
         update(tile, kr, vr);
       }
     }
-    // This wave's part of the next Q^T has landed before the barriers below,
-    // which publish it, and its own copy of Q^T before it parks over it.
-    if (next_staged || own) __builtin_amdgcn_s_waitcnt(0x0F70);
+    // a wave without tiles here still has its copy of the next Q^T in flight
+    if (dma_wait) __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // ---- fold the waves: park in LDS, combine in a fixed order ----
     park<ND>(st, s_slot[wave], lane);
     __syncthreads();
-    if (threadIdx.x < 32) {  // per-head max and sum over the waves
-      const int hd = threadIdx.x;
+    // Thread t folds the f32x4 words t, t + NW*64, ... of the slots; all of
+    // them belong to head t % 32, whose max, weights and sum it derives
+    // itself (no separate per-head pass, no extra barrier).
+    {
+      const int hd = threadIdx.x & 31;
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, s_slot[w].m[hd]);
       const float Ms = (M == kNegInf) ? 0.f : M;
+      float f[NW];
       float l = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        l += (s_slot[w].l[hd] + s_slot[w].l[hd + 32]) * fast_exp2(s_slot[w].m[hd] - Ms);
-      s_fold[0][hd] = M;
-      s_fold[1][hd] = l;
-    }
-    __syncthreads();
-    float* rec = a.records + ((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * a.rec_floats;
-    for (int e = threadIdx.x; e < kWords; e += NW * 64) {
-      const SlotIndex ix(e);
-      const int hd = ix.head();
-      if (hd >= a.hg) continue;
-      const float M = s_fold[0][hd];
-      const float Ms = (M == kNegInf) ? 0.f : M;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < NW; ++w) {
+        f[w] = fast_exp2(s_slot[w].m[hd] - Ms);
+        l += (s_slot[w].l[hd] + s_slot[w].l[hd + 32]) * f[w];
+      }
+      float* rec = a.records + ((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * a.rec_floats;
+      if (hd < a.hg) {
+        for (int e = threadIdx.x; e < kWords; e += NW * 64) {
+          const SlotIndex ix(e);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        acc += s_slot[w].o[ix.blk][ix.r4][ix.lane] * fast_exp2(s_slot[w].m[hd] - Ms);
-      if (complete) {
-        const float inv = 1.0f / s_fold[1][hd];
-        T* op = reinterpret_cast<T*>(a.o) + ((size_t)b_cur * a.h + (size_t)g * a.hg + hd) * DH + ix.d();
-        store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-      } else {
-        *reinterpret_cast<f32x4*>(rec + (size_t)hd * DH + ix.d()) = acc;
-        if (ix.blk == 0 && ix.r4 == 0 && ix.lane < 32) {
-          rec[(size_t)a.hg * DH + hd] = M;
-          rec[(size_t)a.hg * DH + a.hg + hd] = s_fold[1][hd];
+          for (int w = 0; w < NW; ++w) acc += s_slot[w].o[ix.blk][ix.r4][ix.lane] * f[w];
+          if (complete) {
+            const float inv = 1.0f / l;
+            T* op = reinterpret_cast<T*>(a.o) + ((size_t)b_cur * a.h + (size_t)g * a.hg + hd) * DH +
+                    ix.d();
+            store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+          } else {
+            *reinterpret_cast<f32x4*>(rec + (size_t)hd * DH + ix.d()) = acc;
+            if (e < 32) {
+              rec[(size_t)a.hg * DH + hd] = M;
+              rec[(size_t)a.hg * DH + a.hg + hd] = l;
+            }
+          }
         }
       }
     }
