@@ -441,6 +441,9 @@ def main():
                     help="append with mqa_kv_append, then mqa_decode (two launches per step)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
                     help="also run 3 plain device copies of MB MiB (calibrates profiler byte counters)")
+    ap.add_argument("--only", choices=["c2", "c4", "c5", "encdec", "beam4"],
+                    help="run just this secondary workload and print its numbers (for profiling "
+                         "one workload alone); no headline line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -466,6 +469,22 @@ def main():
         torch.cuda.synchronize()
         log(f"probe copy: 3 x {args.probe_copy} MiB read + written")
         del src, dst
+
+    if args.only:
+        steps = args.steps if args.steps != ap.get_default("steps") else None
+        run = {
+            "c2": lambda: decode_result(DecodeBench(W.C2, 64, torch, mqa), steps or 640, 64,
+                                        use_graph),
+            "c4": lambda: decode_result(DecodeBench(W.C4, 1, torch, mqa), steps or 30, 3,
+                                        use_graph),
+            "c5": lambda: prefill_result(W.C5, steps or 10, torch, mqa),
+            "encdec": lambda: attend_result(W.ENCDEC, steps or 10, torch, mqa),
+            "beam4": lambda: beam_result(W.BEAM4, steps or 96, torch, mqa),
+        }[args.only]
+        r = run()
+        print(json.dumps({"only": args.only, **{k: (round(v, 4) if isinstance(v, float) else v)
+                                               for k, v in r.items()}}), flush=True)
+        return
 
     log("headline: serving decode c3 (b=64, h=32, G=1, d_h=128, lens U[1,8192] + append)")
     head = DecodeBench(W.C3, args.rotate, torch, mqa, fused=not args.two_call)
