@@ -157,12 +157,17 @@ __device__ __forceinline__ int wg_of(int64_t t, int64_t T, int W) {
   return (int)(((t + 1) * W + T - 1) / T) - 1;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  // Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round
+  // trips): shifts by 1, 2, 4, 8 within each row of 16 lanes (0 shifted in),
+  // then the last lane of row 0 / 2 is added to row 1 / 3 and the last lane
+  // of row 1 to rows 2 and 3.
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // ---- schedule (each wave on its own) ----
   // Units of sequence b per group: tiles + kSegLead, or 0 when empty.
   // raw0: lens entry of sequence `lane` (the first 64), reused below.
-  int total = 0, nonempty = 0, raw0 = 0;
+  int total = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
   for (int c = 0; c < a.b; c += 64) {
     int raw = 0, v = 0;
     if (c + lane < a.b) {
@@ -341,8 +346,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       v = tiles_of(seq_view_raw(a, raw));
       v = v > 0 ? v + kSegLead : 0;
     }
-    if (c == 0) raw0 = raw;
-    const int incl = wave_incl_scan(v, lane);
+    const int incl = wave_incl_scan(v);
+    if (c == 0) {  // kept for the search below
+      raw0 = raw;
+      v0 = v;
+      incl0 = incl;
+    }
     if (blockIdx.x == 0 && wave == 0 && c + lane < a.b) a.prefix[c + lane] = total + incl - v;
     total += __shfl(incl, 63, 64);
     nonempty += __popcll(__ballot(v > 0));
@@ -368,11 +377,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if (t0 < t1) {
     int run = 0;
     for (int c = 0; c < a.b; c += 64) {
-      int raw = raw0, v = 0;
-      if (c > 0) raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
-      if (c + lane < a.b) v = tiles_of(seq_view_raw(a, raw));
-      v = v > 0 ? v + kSegLead : 0;
-      const int incl = wave_incl_scan(v, lane);
+      int raw = raw0, v = v0, incl = incl0;
+      if (c > 0) {
+        raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
+        v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
+        v = v > 0 ? v + kSegLead : 0;
+        incl = wave_incl_scan(v);
+      }
       const int64_t lo = (int64_t)(run + incl - v) * a.G, hi = (int64_t)(run + incl) * a.G;
       const uint64_t hit = __ballot(c + lane < a.b && v > 0 && lo <= t0 && t0 < hi);
       if (hit) {
