@@ -424,6 +424,46 @@ def cpu_baseline(budget_s=12.0):
                 kv_gbps=kv / dt / 1e9, seconds=dt)
 
 
+# ------------------------------------------------------------------- ceilings
+
+
+def measured_ceilings(torch, mqa):
+    """Practical ceilings measured on this GPU, next to the vendor peaks: the
+    HBM read rate of a plain streaming kernel over 1 GiB (mqa_read_probe), and
+    the bf16 rate of a large torch.matmul (8192^3)."""
+    dev = torch.device("cuda")
+    out = {}
+    buf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)          # 1 GiB
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        mqa.read_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        mqa.read_probe(buf, sink)
+    e1.record()
+    e1.synchronize()
+    out["read_probe_gbps"] = round(buf.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del buf
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    e1.synchronize()
+    out["torch_bf16_matmul_tflops"] = round(2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12,
+                                            1)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 
@@ -502,6 +542,13 @@ def main():
     del head
     torch.cuda.empty_cache()
 
+    log("measured ceilings: streaming read of 1 GiB, bf16 torch.matmul 8192^3")
+    ceil = measured_ceilings(torch, mqa)
+    ceil["kv_frac_of_read_probe"] = round(res["kv_gbps"] / ceil["read_probe_gbps"], 4)
+    ceil["decode_kernel_frac_of_read_probe"] = round(achieved / ceil["read_probe_gbps"], 4)
+    log(f"read probe {ceil['read_probe_gbps']} GB/s, bf16 matmul {ceil['torch_bf16_matmul_tflops']} "
+        f"TFLOP/s")
+
     extra = {}
     if not args.no_extra:
         log("c2 MQA vs MHA comparison point")
@@ -520,11 +567,15 @@ def main():
         log("c5 causal prefill")
         extra["c5_prefill_b4_n4096"] = {k: round(v, 4) if isinstance(v, float) else v
                                         for k, v in prefill_result(W.C5, 10, torch, mqa).items()}
+        extra["c5_prefill_b4_n4096"]["frac_of_torch_bf16_matmul"] = round(
+            extra["c5_prefill_b4_n4096"]["tflops"] / ceil["torch_bf16_matmul_tflops"], 4)
         torch.cuda.empty_cache()
         log("encoder-decoder attention: non-causal over a fixed memory, key-padding mask")
         extra["encdec_b4_n4096_m4096"] = {k: round(v, 4) if isinstance(v, float) else v
                                           for k, v in attend_result(W.ENCDEC, 10, torch,
                                                                     mqa).items()}
+        extra["encdec_b4_n4096_m4096"]["frac_of_torch_bf16_matmul"] = round(
+            extra["encdec_b4_n4096_m4096"]["tflops"] / ceil["torch_bf16_matmul_tflops"], 4)
         torch.cuda.empty_cache()
         log("beam-4 step: reorder + fused append + decode, 16 sources x 4 beams")
         extra["beam4_b16x4_ragged8k"] = {k: round(v, 4) if isinstance(v, float) else v
@@ -559,6 +610,7 @@ def main():
         "kv_gbps": round(res["kv_gbps"], 1),
         "kv_frac_of_hbm_peak": round(res["kv_frac_of_peak"], 4),
         "roofline": roofline,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -187,6 +187,14 @@ int mqa_attend(const void* Q, const void* K, const void* V, int32_t b, int32_t n
  * MQA_ERR_LENS if any lens[b] lies outside [0, m_cap], else MQA_OK. */
 int mqa_check_lens(const int32_t* lens, int32_t b, int32_t m_cap, void* stream);
 
+/* Measurement aid, not part of the attention path: reads `bytes` (a
+ * multiple of 16; buf 16-byte aligned) of device memory once with a plain
+ * streaming kernel, so a caller can time the practical HBM read rate the
+ * decode is compared with.  `sink` is 4 bytes of device memory that is
+ * written only when the XOR of everything read equals 0x5a5aa5a5 (never for
+ * a zero- or one-filled buffer).  One launch on `stream`. */
+int mqa_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* mqa_strerror(int status);
 

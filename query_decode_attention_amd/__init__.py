@@ -34,7 +34,7 @@ _DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
 # Symbols include/mqa.h declares (tests check the library exports each one).
 EXPORTED = ("mqa_kv_append", "mqa_kv_reorder", "mqa_decode_workspace_size",
             "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal", "mqa_attend",
-            "mqa_check_lens", "mqa_strerror", "mqa_abi_version")
+            "mqa_check_lens", "mqa_read_probe", "mqa_strerror", "mqa_abi_version")
 
 
 class MQAError(RuntimeError):
@@ -71,6 +71,7 @@ def _load():
         "mqa_attend": ([P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, ctypes.c_int64,
                         ctypes.c_int64, ctypes.c_int64, P, P], ctypes.c_int),
         "mqa_check_lens": ([P, I32, I32, P], ctypes.c_int),
+        "mqa_read_probe": ([P, SZ, P, P], ctypes.c_int),
         "mqa_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "mqa_abi_version": ([], ctypes.c_int),
     }
@@ -325,6 +326,15 @@ def check_lens(lens, m_cap):
     """Synchronising host check that every lens[b] lies in [0, m_cap]."""
     dev = _dev(lens)
     _check("mqa_check_lens", _lib.mqa_check_lens(_ptr(lens), lens.numel(), int(m_cap),
+                                                 _stream(dev)))
+
+
+def read_probe(buf, sink):
+    """Stream-read the device tensor ``buf`` once (a measurement aid: the
+    practical HBM read rate); ``sink`` is a 4-byte device tensor."""
+    dev = _dev(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check("mqa_read_probe", _lib.mqa_read_probe(_ptr(buf), nbytes - nbytes % 16, _ptr(sink),
                                                  _stream(dev)))
 
 

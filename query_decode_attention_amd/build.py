@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmqa.so")
-SOURCES = ["mqa_api.cpp", "mqa_decode.hip", "mqa_prefill.hip", "mqa_reorder.hip"]
+SOURCES = ["mqa_api.cpp", "mqa_decode.hip", "mqa_prefill.hip", "mqa_reorder.hip", "mqa_probe.hip"]
 ARCH = "gfx950"
 
 

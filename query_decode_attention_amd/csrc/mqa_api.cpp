@@ -77,7 +77,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MQA_OK : MQA_ERR_LAUN
 
 extern "C" {
 
-int mqa_abi_version(void) { return 202; }
+int mqa_abi_version(void) { return 203; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -266,6 +266,14 @@ int mqa_attend(const void* Q, const void* K, const void* V, int32_t b, int32_t n
   a.msh = mask_sh;
   a.msn = mask_sn;
   return launch_status(mqa::launch_attend(a, static_cast<hipStream_t>(stream)));
+}
+
+int mqa_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return MQA_ERR_NULL;
+  if (!aligned16(buf) || bytes % 16 != 0) return MQA_ERR_ALIGN;
+  if (bytes == 0) return MQA_OK;
+  return launch_status(mqa::launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink),
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int mqa_check_lens(const int32_t* lens, int32_t b, int32_t m_cap, void* stream) {

@@ -64,6 +64,7 @@ size_t decode_workspace_bytes(int b, int h, int G, int dh, int m_cap);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int current_device_cus(int* device_out);

@@ -42,6 +42,7 @@ def lib(libmqa_path):
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
     L.mqa_kv_reorder.argtypes = [CP, P, P, I32, P, P]
+    L.mqa_read_probe.argtypes = [P, SZ, P, P]
     L64 = ctypes.c_int64
     L.mqa_attend.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, L64, L64, L64,
                              P, P]
@@ -60,7 +61,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
         "mqa_decode_ex", "mqa_decode_workspace_size",
-        "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_strerror"])
+        "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_read_probe",
+        "mqa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib, libmqa_path):
@@ -76,7 +78,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 202
+    assert q.abi_version() == 203
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -175,6 +177,15 @@ def test_check_lens_argument_errors(lib):
     assert lib.mqa_check_lens(None, 3, 10, None) == ENULL
     assert lib.mqa_check_lens(FAKE, -1, 10, None) == ESHAPE
     assert lib.mqa_check_lens(None, 0, 10, None) == OK
+
+
+def test_read_probe_rejects_bad_arguments_before_launching(lib):
+    f = lib.mqa_read_probe
+    assert f(None, 1024, FAKE, None) == ENULL
+    assert f(FAKE, 1024, None, None) == ENULL
+    assert f(FAKE_MIS, 1024, FAKE, None) == EALIGN
+    assert f(FAKE, 1000, FAKE, None) == EALIGN              # not a multiple of 16 bytes
+    assert f(FAKE, 0, FAKE, None) == OK                     # nothing to read: nothing launched
 
 
 def test_reorder_rejects_bad_arguments_before_launching(lib):
