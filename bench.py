@@ -303,10 +303,12 @@ def attend_result(cfg, steps, torch, mqa, R=2):
 
 
 def beam_result(cfg, steps, torch, mqa, R=4):
-    """Beam step = mqa_kv_reorder (random parents, ~3/4 of the rows move)
-    followed by the fused append + decode, over R rotated caches, replayed
-    from a HIP graph.  Bytes: the decode's K/V of every hypothesis plus the
-    reorder's moved rows, read and written."""
+    """Beam step = mqa_kv_reorder_to (random parents, ~3/4 of the rows move;
+    the lengths alternate between two arrays per cache) followed by the fused
+    append + decode on the new lengths, over R rotated caches, replayed from
+    a HIP graph of 2R steps (each cache once in each direction).  Bytes: the
+    decode's K/V of every hypothesis plus the reorder's moved rows, read and
+    written."""
     dev = torch.device("cuda")
     b, h, G, dh, m_cap, beam = cfg.b, cfg.h, cfg.G, cfg.dh, cfg.m_cap, cfg.beam
     elem = 2 if cfg.dtype == torch.bfloat16 else 4
@@ -320,7 +322,8 @@ def beam_result(cfg, steps, torch, mqa, R=4):
         src_lens = torch.randint(cfg.lens_lo, cfg.lens_hi + 1, (cfg.sources,), generator=gc,
                                  dtype=torch.int64)
         parent = torch.randint(0, beam, (b,), generator=gc, dtype=torch.int64).to(torch.int32)
-        c = dict(K=K, V=V, lens=src_lens.repeat_interleave(beam).to(torch.int32).to(dev),
+        lens0 = src_lens.repeat_interleave(beam).to(torch.int32).to(dev)
+        c = dict(K=K, V=V, lens=[lens0, torch.empty_like(lens0)],
                  parent=parent.to(dev),
                  q=torch.randn(b, h, dh, generator=gg, device=dev).to(cfg.dtype),
                  kn=torch.randn(b, G, dh, generator=gg, device=dev).to(cfg.dtype),
@@ -332,13 +335,15 @@ def beam_result(cfg, steps, torch, mqa, R=4):
                           if int(parent[i]) != i % beam) for s_i in range(cfg.sources)])
     out = torch.empty(b, h, dh, dtype=cfg.dtype, device=dev)
     ws = mqa.workspace_for(h, copies[0]["K"])
-    dsteps = [mqa.DecodeStep(c["q"], c["K"], c["V"], c["lens"], cfg.scale, out=out,
-                             workspace=ws, k_new=c["kn"], v_new=c["vn"]) for c in copies]
+    dsteps = [[mqa.DecodeStep(c["q"], c["K"], c["V"], c["lens"][ph], cfg.scale, out=out,
+                              workspace=ws, k_new=c["kn"], v_new=c["vn"]) for ph in range(2)]
+              for c in copies]
 
-    def step(r):
+    def step(r, ph):
+        """Reorder lens[ph] -> lens[1 - ph], then append + decode on lens[1 - ph]."""
         c = copies[r]
-        mqa.kv_reorder(c["K"], c["V"], c["lens"], c["parent"], beam)
-        dsteps[r]()
+        mqa.kv_reorder(c["K"], c["V"], c["lens"][ph], c["parent"], beam, lens_out=c["lens"][1 - ph])
+        dsteps[r][1 - ph]()
 
     appends = [0] * R
 
@@ -352,36 +357,39 @@ def beam_result(cfg, steps, torch, mqa, R=4):
             mv += moved[r][s_i] * L_pre
         return rd, 2 * 2 * mv * row               # moved rows: read + write, K and V
 
-    for i in range(2 * R):                         # warm-up
-        step(i % R)
-        appends[i % R] += 1
+    for ph in range(2):                            # warm-up: two steps per cache
+        for r in range(R):
+            step(r, ph)
+            appends[r] += 1
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(st):
         with torch.cuda.graph(g, stream=st):
-            for r in range(R):
-                step(r)
+            for ph in range(2):
+                for r in range(R):
+                    step(r, ph)
     torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
-    n_rep = max(1, math.ceil(steps / R))
-    # the capture itself ran one step per copy
+    n_rep = max(1, math.ceil(steps / (2 * R)))
+    # the capture itself ran two steps per copy
     for r in range(R):
-        appends[r] += 1
+        appends[r] += 2
     kv = mvb = 0
     for k in range(n_rep):
-        for r in range(R):
-            a, m = step_bytes(r, appends[r] + k)
-            kv += a
-            mvb += m
+        for j in range(2):
+            for r in range(R):
+                a, m = step_bytes(r, appends[r] + 2 * k + j)
+                kv += a
+                mvb += m
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(n_rep):
         g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    n = n_rep * R
+    n = n_rep * 2 * R
     return dict(ms_per_step=1e3 * dt / n, steps_per_s=n / dt,
                 us_per_output_token=1e6 * dt / n / cfg.sources,
                 kv_gbps=kv / dt / 1e9, reorder_gbps=mvb / dt / 1e9,

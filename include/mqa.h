@@ -100,6 +100,16 @@ int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache,
 int mqa_kv_reorder(const mqa_cache* cache, int32_t* lens, const int32_t* parent, int32_t beam,
                    int32_t* err_flag, void* stream);
 
+/* mqa_kv_reorder_to -- mqa_kv_reorder with the permuted lengths written to a
+ * separate array: lens_out[i] = lens_in[src(i)] (lens_out[i] = lens_in[i]
+ * for a bad parent), K and V rows reordered in place exactly as above.
+ * lens_in is only read, so one launch suffices; a beam loop alternates two
+ * lens arrays (reorder from one into the other, then mqa_append_decode on
+ * the other).  lens_out must not overlap lens_in (equal pointers:
+ * MQA_ERR_SHAPE); other arguments and errors as for mqa_kv_reorder. */
+int mqa_kv_reorder_to(const mqa_cache* cache, const int32_t* lens_in, int32_t* lens_out,
+                      const int32_t* parent, int32_t beam, int32_t* err_flag, void* stream);
+
 /* Bytes of device workspace a decode needs for `h` query heads over `cache`:
  * a small schedule header (b + 1 ints) followed by the split-K partial
  * results.  Depends only on the shapes, never on the device or on lens.

@@ -32,7 +32,7 @@ MQA_F32, MQA_BF16 = 0, 1
 _DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
 
 # Symbols include/mqa.h declares (tests check the library exports each one).
-EXPORTED = ("mqa_kv_append", "mqa_kv_reorder", "mqa_decode_workspace_size",
+EXPORTED = ("mqa_kv_append", "mqa_kv_reorder", "mqa_kv_reorder_to", "mqa_decode_workspace_size",
             "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal", "mqa_attend",
             "mqa_check_lens", "mqa_read_probe", "mqa_strerror", "mqa_abi_version")
 
@@ -62,6 +62,7 @@ def _load():
     sig = {
         "mqa_kv_append": ([P, P, CP, P, P, P], ctypes.c_int),
         "mqa_kv_reorder": ([CP, P, P, I32, P, P], ctypes.c_int),
+        "mqa_kv_reorder_to": ([CP, P, P, P, I32, P, P], ctypes.c_int),
         "mqa_decode_workspace_size": ([I32, CP], SZ),
         "mqa_decode": ([P, I32, CP, P, F, I32, P, P, SZ, P], ctypes.c_int),
         "mqa_append_decode": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P], ctypes.c_int),
@@ -186,21 +187,30 @@ def kv_append(k_new, v_new, K, V, lens, err_flag=None):
                                                  _ptr(lens), _ptr(err_flag), _stream(dev)))
 
 
-def kv_reorder(K, V, lens, parent, beam: int, err_flag=None):
-    """Beam reorder in place (async): hypothesis i takes the cached rows and
-    the length of hypothesis (i // beam) * beam + parent[i].
+def kv_reorder(K, V, lens, parent, beam: int, err_flag=None, lens_out=None):
+    """Beam reorder (async): hypothesis i takes the cached rows and the length
+    of hypothesis (i // beam) * beam + parent[i].  K and V are reordered in
+    place; the lengths too, or, with ``lens_out``, into that tensor (lens
+    only read; one launch instead of two).
 
-    K, V: [b, m_cap, G, d_h]; lens, parent: int32 [b] on the same device."""
-    dev = _dev(K, V, lens, parent, err_flag)
+    K, V: [b, m_cap, G, d_h]; lens, parent, lens_out: int32 [b] on the same device."""
+    dev = _dev(K, V, lens, parent, err_flag, lens_out)
     b = K.shape[0]
-    for name, t in (("lens", lens), ("parent", parent)):
+    named = [("lens", lens), ("parent", parent)] + ([("lens_out", lens_out)] if lens_out is not None
+                                                     else [])
+    for name, t in named:
         if t.dtype != torch.int32 or t.shape != (b,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 tensor of shape [{b}]")
     if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1):
         raise ValueError("err_flag must be an int32 tensor")
     c = _cache(K, V)
-    _check("mqa_kv_reorder", _lib.mqa_kv_reorder(ctypes.byref(c), _ptr(lens), _ptr(parent),
-                                                   int(beam), _ptr(err_flag), _stream(dev)))
+    if lens_out is None:
+        _check("mqa_kv_reorder", _lib.mqa_kv_reorder(ctypes.byref(c), _ptr(lens), _ptr(parent),
+                                                       int(beam), _ptr(err_flag), _stream(dev)))
+    else:
+        _check("mqa_kv_reorder_to", _lib.mqa_kv_reorder_to(
+            ctypes.byref(c), _ptr(lens), _ptr(lens_out), _ptr(parent), int(beam), _ptr(err_flag),
+            _stream(dev)))
 
 
 def decode_workspace_size(h: int, K) -> int:

@@ -73,11 +73,34 @@ int check_heads(int32_t h, int32_t G) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MQA_OK : MQA_ERR_LAUNCH; }
 
+// In place (lens_out null, two launches) or into lens_out (one launch).
+int kv_reorder(const mqa_cache* cache, int32_t* lens, int32_t* lens_out, bool out_of_place,
+               const int32_t* parent, int32_t beam, int32_t* err_flag, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != MQA_OK) return rc;
+  if (beam < 1 || beam > mqa::kMaxBeam || cache->b % beam != 0) return MQA_ERR_SHAPE;
+  if (cache->b == 0) return MQA_OK;
+  if (!lens || !parent || (out_of_place && !lens_out)) return MQA_ERR_NULL;
+  if (out_of_place && lens_out == lens) return MQA_ERR_SHAPE;
+  mqa::ReorderParams p;
+  p.k = static_cast<char*>(cache->k);
+  p.v = static_cast<char*>(cache->v);
+  p.lens = lens;
+  p.lens_out = lens_out;
+  p.parent = parent;
+  p.err_flag = err_flag;
+  p.b = cache->b;
+  p.m_cap = cache->m_cap;
+  p.beam = beam;
+  p.row_bytes = cache->G * cache->d_h * elem_size(cache->dtype);
+  return launch_status(mqa::launch_kv_reorder(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
 
-int mqa_abi_version(void) { return 203; }
+int mqa_abi_version(void) { return 204; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -114,24 +137,16 @@ int mqa_kv_append(const void* k_new, const void* v_new, const mqa_cache* cache, 
   return launch_status(mqa::launch_kv_append(p, static_cast<hipStream_t>(stream)));
 }
 
+
 int mqa_kv_reorder(const mqa_cache* cache, int32_t* lens, const int32_t* parent, int32_t beam,
                    int32_t* err_flag, void* stream) {
-  int rc = check_cache(cache);
-  if (rc != MQA_OK) return rc;
-  if (beam < 1 || beam > mqa::kMaxBeam || cache->b % beam != 0) return MQA_ERR_SHAPE;
-  if (cache->b == 0) return MQA_OK;
-  if (!lens || !parent) return MQA_ERR_NULL;
-  mqa::ReorderParams p;
-  p.k = static_cast<char*>(cache->k);
-  p.v = static_cast<char*>(cache->v);
-  p.lens = lens;
-  p.parent = parent;
-  p.err_flag = err_flag;
-  p.b = cache->b;
-  p.m_cap = cache->m_cap;
-  p.beam = beam;
-  p.row_bytes = cache->G * cache->d_h * elem_size(cache->dtype);
-  return launch_status(mqa::launch_kv_reorder(p, static_cast<hipStream_t>(stream)));
+  return kv_reorder(cache, lens, nullptr, false, parent, beam, err_flag, stream);
+}
+
+int mqa_kv_reorder_to(const mqa_cache* cache, const int32_t* lens_in, int32_t* lens_out,
+                      const int32_t* parent, int32_t beam, int32_t* err_flag, void* stream) {
+  return kv_reorder(cache, const_cast<int32_t*>(lens_in), lens_out, true, parent, beam, err_flag,
+                    stream);
 }
 
 size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache) {

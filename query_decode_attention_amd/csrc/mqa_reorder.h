@@ -11,7 +11,8 @@ constexpr int kMaxBeam = 16;
 struct ReorderParams {
   char* k;
   char* v;
-  int32_t* lens;
+  int32_t* lens;           // read; permuted in place when lens_out is null
+  int32_t* lens_out;       // nullable: the permuted lengths go here instead
   const int32_t* parent;  // beam-local parent of every hypothesis
   int32_t* err_flag;      // nullable
   int b, m_cap, beam;

@@ -16,8 +16,10 @@
 // Consecutive lanes take consecutive chunks of consecutive positions: every
 // load and store instruction of a wave covers whole rows.
 //
-// lens is rewritten by a second, one-workgroup kernel afterwards (every block
-// of the first kernel reads the old lengths).
+// In place, lens is rewritten by a second, one-workgroup kernel afterwards
+// (every block of the first kernel reads the old lengths).  With a separate
+// output array the first block of each group writes the group's permuted
+// lengths there, and there is no second launch.
 #include "mqa_device.h"
 #include "mqa_reorder.h"
 
@@ -58,6 +60,11 @@ __global__ __launch_bounds__(256) void reorder_rows_kernel(ReorderParams p) {
       src[i] = __builtin_amdgcn_readfirstlane(src[i]);
       len[i] = __builtin_amdgcn_readfirstlane(len[i]);
       span = len[i] > span ? len[i] : span;
+    }
+    if (p.lens_out && blockIdx.x == 0 && (int)threadIdx.x < p.beam) {
+      const int i = base + (int)threadIdx.x;
+      const int par = p.parent[i];
+      p.lens_out[i] = (par >= 0 && par < p.beam) ? p.lens[base + par] : p.lens[i];
     }
     if (pos >= span) continue;
     for (int half = 0; half < 2; ++half) {
@@ -118,7 +125,7 @@ hipError_t launch_kv_reorder(const ReorderParams& p, hipStream_t s) {
   else
     hipLaunchKernelGGL(reorder_rows_kernel<kMaxBeam>, dim3(gx, gy), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.lens_out) return e;
   hipLaunchKernelGGL(reorder_lens_kernel, dim3(1), dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -42,6 +42,7 @@ def lib(libmqa_path):
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
     L.mqa_kv_reorder.argtypes = [CP, P, P, I32, P, P]
+    L.mqa_kv_reorder_to.argtypes = [CP, P, P, P, I32, P, P]
     L.mqa_read_probe.argtypes = [P, SZ, P, P]
     L64 = ctypes.c_int64
     L.mqa_attend.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, L64, L64, L64,
@@ -61,7 +62,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
         "mqa_decode_ex", "mqa_decode_workspace_size",
-        "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_prefill_causal", "mqa_read_probe",
+        "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_kv_reorder_to", "mqa_prefill_causal",
+        "mqa_read_probe",
         "mqa_strerror"])
 
 
@@ -78,7 +80,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 203
+    assert q.abi_version() == 204
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -186,6 +188,24 @@ def test_read_probe_rejects_bad_arguments_before_launching(lib):
     assert f(FAKE_MIS, 1024, FAKE, None) == EALIGN
     assert f(FAKE, 1000, FAKE, None) == EALIGN              # not a multiple of 16 bytes
     assert f(FAKE, 0, FAKE, None) == OK                     # nothing to read: nothing launched
+
+
+def test_reorder_to_rejects_bad_arguments_before_launching(lib):
+    r = lib.mqa_kv_reorder_to
+    OTHER = ctypes.c_void_p(0x7F0000002000)
+
+    def call(c=None, lens=FAKE, out=OTHER, parent=FAKE, beam=4):
+        c = c if c is not None else cache(b=8)
+        return r(ctypes.byref(c), lens, out, parent, beam, None, None)
+
+    assert r(None, FAKE, OTHER, FAKE, 4, None, None) == ENULL
+    assert call(lens=None) == ENULL
+    assert call(out=None) == ENULL
+    assert call(parent=None) == ENULL
+    assert call(out=FAKE) == ESHAPE                     # lens_out == lens_in
+    assert call(beam=3) == ESHAPE
+    assert call(c=cache(b=8, dh=96)) == EDHEAD
+    assert call(c=cache(b=0)) == OK                     # nothing to reorder
 
 
 def test_reorder_rejects_bad_arguments_before_launching(lib):

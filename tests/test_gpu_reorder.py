@@ -129,3 +129,61 @@ def test_beam_steps_small(dtype):
 def test_beam_steps_full_beam4():
     cfg = W.BEAM4
     run_beam_steps(cfg, W.beam_inputs(cfg, steps=2), 2)
+
+
+@pytest.mark.parametrize("dtype,b,beam,G,dh,m_cap", GRID[:5])
+def test_reorder_to_equals_in_place(dtype, b, beam, G, dh, m_cap):
+    """Out-of-place lengths: the same cache bytes as the in-place reorder,
+    lens_out equal to the in-place lens, lens_in untouched, the same flag."""
+    what = f"reorder_to {dtype} b={b} beam={beam} G={G} dh={dh} m_cap={m_cap}"
+    announce(what)
+    K, V, g = cache(dtype, b, m_cap, G, dh, 350 + b + m_cap)
+    lens = torch.randint(0, m_cap + 1, (b,), generator=g, dtype=torch.int32)
+    parent = torch.randint(0, beam, (b,), generator=g, dtype=torch.int32)
+    parent[b - 1] = beam + 2                                   # one bad parent
+    runs = []
+    for out_of_place in (False, True):
+        dK, dV, dl, dp = K.cuda(), V.cuda(), lens.cuda(), parent.cuda()
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        lo = torch.full((b,), -7, dtype=torch.int32, device="cuda") if out_of_place else None
+        mqa.kv_reorder(dK, dV, dl, dp, beam, err_flag=flag, lens_out=lo)
+        torch.cuda.synchronize()
+        runs.append((raw(dK.cpu()), raw(dV.cpu()), dl.cpu(), None if lo is None else lo.cpu(),
+                     int(flag.item())))
+    (k0, v0, l0, _, f0), (k1, v1, lin, lout, f1) = runs
+    assert k0.tobytes() == k1.tobytes() and v0.tobytes() == v1.tobytes(), what
+    assert torch.equal(lout, l0), what
+    assert torch.equal(lin, lens), what
+    assert f0 == f1 == 1, what
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_beam_steps_ping_pong_lens(dtype):
+    """Beam steps with the lengths alternating between two arrays
+    (reorder_to, then fused append + decode on the new one) against the
+    oracle's reorder, append and decode."""
+    cfg = W.BeamConfig("beam_pp", dtype, sources=3, beam=4, h=8, G=2, dh=64, m_cap=200,
+                       lens_lo=1, lens_hi=150, seed=360)
+    steps = 4
+    inp = W.beam_inputs(cfg, steps=steps)
+    d = {k: v.cuda() for k, v in inp.items()}
+    lens = [d["lens"], torch.empty_like(d["lens"])]
+    Kr, Vr, lr = raw(inp["K"]), raw(inp["V"]), inp["lens"].numpy().copy()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s in range(steps):
+        announce(f"ping-pong beam step {s}")
+        src, dst = lens[s % 2], lens[1 - s % 2]
+        mqa.kv_reorder(d["K"], d["V"], src, d["parent"][s].contiguous(), cfg.beam, err_flag=flag,
+                       lens_out=dst)
+        o = mqa.append_decode(d["q"][s].contiguous(), d["k_new"][s].contiguous(),
+                              d["v_new"][s].contiguous(), d["K"], d["V"], dst, cfg.scale,
+                              err_flag=flag)
+        torch.cuda.synchronize()
+        oracle.kv_reorder(Kr, Vr, lr, inp["parent"][s].numpy(), cfg.beam)
+        oracle.kv_append(inp["k_new"][s], inp["v_new"][s], Kr, Vr, lr)
+        ref = oracle.decode(inp["q"][s], Kr, Vr, lr, cfg.scale)
+        assert_parity(o, ref, cfg.dtype, f"{cfg.name} step {s}")
+        assert np.array_equal(dst.cpu().numpy(), lr)
+    assert int(flag.item()) == 0
+    assert raw(d["K"].cpu()).tobytes() == Kr.tobytes()
+    assert raw(d["V"].cpu()).tobytes() == Vr.tobytes()
