@@ -16,14 +16,17 @@
 // w of a grid of W takes units [U*w/W, U*(w+1)/W): every workgroup streams
 // about the same number of bytes whatever the length mix, a few tiles fewer
 // for each segment boundary its range crosses (see kSegLead).  Each
-// wave derives this schedule from lens by itself (wave-wide scan) and keeps
-// the lens entries it needs in registers, so the schedule costs no host
-// synchronisation, no barrier and one read of lens.
+// wave derives this schedule from lens by itself (a DPP prefix sum over the
+// wave) and keeps the lens entries it needs in registers, so the schedule
+// costs no host synchronisation, no barrier and one read of lens.
 //
-// Q.  A segment's Q^T operand is staged in LDS once for all its tiles.  When
-// a workgroup's range goes on past the current segment, the next segment's
-// Q^T is copied into a second LDS buffer while the current one streams, so
-// the switch to it costs no memory round trip.
+// Q.  A segment's Q^T operand sits in LDS for all its tiles.  In a
+// workgroup's first segment every wave copies it into its own fold slot (free
+// until that wave parks), so the copy shares a round trip with the wave's
+// first tile and no wave waits for another.  When a workgroup's range goes
+// on past the current segment, the next segment's Q^T is copied into a shared
+// LDS buffer while the current one streams, so the switch to it costs no
+// memory round trip.
 //
 // Inside a workgroup, wave k takes every NW-th tile of a segment.  At the end
 // of a segment all waves park their (max, sum, accumulator) in LDS and the
