@@ -373,9 +373,7 @@ def beam_result(cfg, steps, torch, mqa, R=4):
     torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
     n_rep = max(1, math.ceil(steps / (2 * R)))
-    # the capture itself ran two steps per copy
-    for r in range(R):
-        appends[r] += 2
+    # (capturing records the steps without running them: appends unchanged)
     kv = mvb = 0
     for k in range(n_rep):
         for j in range(2):
