@@ -244,6 +244,43 @@ def test_mqa_equals_tied_mha_on_gpu():
     assert_parity(o2, ref, torch.bfloat16, "tied mha")
 
 
+def test_permuted_cache_positions_give_the_same_output():
+    """P10 on the GPU: the core has no positional term, so permuting the
+    visible positions of every sequence (K and V together) changes only the
+    summation order."""
+    announce("position permutation invariance")
+    cfg, inp = make(torch.bfloat16, 4, 32, 1, 128, 600, 40, 600, seed=7415)
+    o1, _ = run_decode(inp, cfg.scale)
+    g = torch.Generator().manual_seed(7416)
+    perm = dict(inp)
+    perm["K"], perm["V"] = inp["K"].clone(), inp["V"].clone()
+    for bi, L in enumerate(inp["lens"].tolist()):
+        p = torch.randperm(L, generator=g)
+        perm["K"][bi, :L] = inp["K"][bi, p]
+        perm["V"][bi, :L] = inp["V"][bi, p]
+    o2, _ = run_decode(perm, cfg.scale)
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o1, ref, torch.bfloat16, "original order")
+    assert_parity(o2, ref, torch.bfloat16, "permuted positions")
+
+
+def test_gqa_endpoints_equal_per_head_mqa():
+    """P7 on the GPU: with G = h every head has its own K/V head (the MHA
+    route); it must equal h single-head MQA decodes over that head's K/V."""
+    announce("G = h vs per-head G = 1")
+    cfg, inp = make(torch.bfloat16, 3, 8, 8, 64, 300, 50, 300, seed=7417)
+    o_all, _ = run_decode(inp, cfg.scale)
+    for i in range(cfg.h):
+        one = {"q": inp["q"][:, i:i + 1].contiguous(),
+               "K": inp["K"][:, :, i:i + 1].contiguous(),
+               "V": inp["V"][:, :, i:i + 1].contiguous(),
+               "lens": inp["lens"]}
+        o_i, _ = run_decode(one, cfg.scale)
+        ref, _ = oracle_step(one, cfg.scale)
+        assert_parity(o_i, ref, torch.bfloat16, f"head {i} as MQA")
+        assert_parity(o_all[:, i:i + 1], ref, torch.bfloat16, f"head {i} within G = h")
+
+
 def test_append_is_bit_exact_and_flags_full_caches():
     announce("append bit-exact")
     cfg, inp = make(torch.bfloat16, 5, 32, 2, 128, 64, 0, 64, seed=7420)
