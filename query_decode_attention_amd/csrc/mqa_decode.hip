@@ -12,7 +12,7 @@
 //
 // Work decomposition.  The visible positions of every (sequence b, group g)
 // segment are cut into tiles of 32.  All segments form one flat list of U
-// units -- kSegLead lead-in units, then the segment's tiles -- and workgroup
+// units -- a few lead-in units, then the segment's tiles -- and workgroup
 // w of a grid of W takes units [U*w/W, U*(w+1)/W): every workgroup streams
 // about the same number of bytes whatever the length mix, a few tiles fewer
 // for each segment boundary its range crosses (see kSegLead).  Each
@@ -97,8 +97,9 @@ struct DecodeArgs {
   int32_t* err_flag;     // nullable
   char* o;
   float* records;        // [2 * grid][rec_floats] partial results
-  int32_t* prefix;       // [b + 1] tiles before each sequence, then the count of
-                         // non-empty sequences (written by workgroup 0)
+  int32_t* prefix;       // [b + 1] units before each sequence, then the count of
+                         // non-empty sequences, the lead-in and the effective
+                         // grid (written by workgroup 0 for the combine)
   int b, h, G, hg, m_cap, window;
   int rec_floats;
   float scale_log2;
@@ -132,25 +133,37 @@ __device__ __forceinline__ int tiles_of(const SeqView& s) {
   return (s.L - s.j0 + kTileRows - 1) / kTileRows;
 }
 
-// Schedule units.  Every non-empty segment is kSegLead virtual units (no
+// Schedule units.  Every non-empty segment is `lead` virtual units (no
 // positions) followed by its tiles, and workgroups split the units evenly.  A
 // workgroup whose range reaches into a further segment thereby takes about
-// kSegLead fewer tiles, which pays for the fold at the segment boundary (the
+// `lead` fewer tiles, which pays for the fold at the segment boundary (the
 // waves of a workgroup meet there, so its critical path grows by about half
-// a round of tiles per boundary crossed).
+// a round of tiles per boundary crossed).  A small step (at most one tile per
+// wave of the launched grid) has no lead-in and up to one workgroup per
+// kSmallUnits units: there every workgroup has about one round of loads, a
+// CU streams only ~20 GB/s, and spreading the step over more CUs is worth
+// more than avoiding boundaries.
 constexpr int kSegLead = 6;
+constexpr int kSmallUnits = 4;
 
 // Workgroups that share the Tv units of `segs` non-empty segments: the
-// launched grid, but no more than one per `min_tiles` units unless there are
+// launched grid, but no more than one per `min_units` units unless there are
 // more segments than that (short segments are better run side by side than
-// one after another), and no more than Tv / (kSegLead + 1), so that every
-// range of units holds at least one tile.  Both kernels derive the same value.
-__device__ __forceinline__ int effective_grid(int64_t Tv, int64_t segs, int grid, int min_tiles) {
-  int64_t w = (Tv + min_tiles - 1) / min_tiles;
+// one after another), and no more than Tv / (lead + 1), so that every range
+// of units holds at least one tile.  The combine reads the value back.
+__device__ __forceinline__ int effective_grid(int64_t Tv, int64_t segs, int grid, int min_units,
+                                             int lead) {
+  int64_t w = (Tv + min_units - 1) / min_units;
   if (w < segs) w = segs;
   if (w > grid) w = grid;
-  if (w > Tv / (kSegLead + 1)) w = Tv / (kSegLead + 1);
+  if (w > Tv / (lead + 1)) w = Tv / (lead + 1);
   return (int)(w < 1 ? 1 : w);
+}
+
+// Lanes below this one whose bit is set in `mask` (a wave-wide ballot).
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // First unit of workgroup w out of W over T units.
@@ -339,38 +352,63 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   u32x4 (*const own_q)[64] = reinterpret_cast<u32x4 (*)[64]>(&s_slot[wave]);
 
   // ---- schedule (each wave on its own) ----
-  // Units of sequence b per group: tiles + kSegLead, or 0 when empty.
-  // raw0: lens entry of sequence `lane` (the first 64), reused below.
-  int total = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
+  // Pass 1: tiles of every sequence (per group) and the non-empty count,
+  // which fix the lead-in.  raw0 / v0 / incl0: lens entry, tiles and their
+  // inclusive prefix for sequence `lane` (the first 64), reused below.
+  int tiles = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
   for (int c = 0; c < a.b; c += 64) {
     int raw = 0, v = 0;
     if (c + lane < a.b) {
       raw = a.lens[c + lane];
       v = tiles_of(seq_view_raw(a, raw));
-      v = v > 0 ? v + kSegLead : 0;
     }
     const int incl = wave_incl_scan(v);
-    if (c == 0) {  // kept for the search below
+    if (c == 0) {
       raw0 = raw;
       v0 = v;
       incl0 = incl;
     }
-    if (blockIdx.x == 0 && wave == 0 && c + lane < a.b) a.prefix[c + lane] = total + incl - v;
-    total += __shfl(incl, 63, 64);
+    tiles += __shfl(incl, 63, 64);
     nonempty += __popcll(__ballot(v > 0));
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.prefix[a.b] = total;
-    a.prefix[a.b + 1] = nonempty;
-  }
-  total = __builtin_amdgcn_readfirstlane(total);
+  tiles = __builtin_amdgcn_readfirstlane(tiles);
   nonempty = __builtin_amdgcn_readfirstlane(nonempty);
+  const bool small = (int64_t)tiles * a.G <= (int64_t)NW * gridDim.x;
+  const int lead = small ? 0 : kSegLead;
+  const int total = tiles + lead * nonempty;                // units per group
   const int64_t Tt = (int64_t)total * a.G;                  // units
   const int64_t segs = (int64_t)nonempty * a.G;
   // Workgroups in use (see effective_grid): every wave has work, short
   // segments still run side by side.
-  const int W = effective_grid(Tt, segs, gridDim.x, NW);
+  const int W = effective_grid(Tt, segs, gridDim.x, small ? kSmallUnits : NW, lead);
   const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
+  // Units of the sequences of one chunk: their tiles plus `lead` per non-empty
+  // sequence; u_excl / u_incl are prefixes within the chunk.
+  auto chunk_units = [&](int v, int incl, int& u, int& u_incl) {
+    const uint64_t ne = __ballot(v > 0);
+    u = v > 0 ? v + lead : 0;
+    u_incl = incl + lead * (lanes_below(ne) + (v > 0 ? 1 : 0));
+  };
+  if (blockIdx.x == 0 && wave == 0) {  // the units prefix, for the combine
+    int run = 0;
+    for (int c = 0; c < a.b; c += 64) {
+      int v = v0, incl = incl0;
+      if (c > 0) {
+        v = (c + lane < a.b) ? tiles_of(seq_view(a, c + lane)) : 0;
+        incl = wave_incl_scan(v);
+      }
+      int u, u_incl;
+      chunk_units(v, incl, u, u_incl);
+      if (c + lane < a.b) a.prefix[c + lane] = run + u_incl - u;
+      run += __shfl(u_incl, 63, 64);
+    }
+    if (lane == 0) {
+      a.prefix[a.b] = total;
+      a.prefix[a.b + 1] = nonempty;
+      a.prefix[a.b + 2] = lead;
+      a.prefix[a.b + 3] = W;
+    }
+  }
 
   // lens entries of sequences cbase .. cbase + 63, one per lane: the segment
   // walk below reads lens from here, not from memory.
@@ -384,20 +422,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       if (c > 0) {
         raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
         v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
-        v = v > 0 ? v + kSegLead : 0;
         incl = wave_incl_scan(v);
       }
-      const int64_t lo = (int64_t)(run + incl - v) * a.G, hi = (int64_t)(run + incl) * a.G;
-      const uint64_t hit = __ballot(c + lane < a.b && v > 0 && lo <= t0 && t0 < hi);
+      int u, u_incl;
+      chunk_units(v, incl, u, u_incl);
+      const int64_t lo = (int64_t)(run + u_incl - u) * a.G, hi = (int64_t)(run + u_incl) * a.G;
+      const uint64_t hit = __ballot(c + lane < a.b && u > 0 && lo <= t0 && t0 < hi);
       if (hit) {
         const int src = __builtin_ctzll(hit);
         b_cur = c + src;
-        seg_base = (int64_t)(run + __shfl(incl - v, src, 64)) * a.G;
+        seg_base = (int64_t)(run + __shfl(u_incl - u, src, 64)) * a.G;
         cbase = c;
         craw = raw;
         break;
       }
-      run += __shfl(incl, 63, 64);
+      run += __shfl(u_incl, 63, 64);
     }
     b_cur = __builtin_amdgcn_readfirstlane(b_cur);
   }
@@ -455,15 +494,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       ++b_cur;
       continue;
     }
-    const int unit = nb + kSegLead;  // units of one group of this sequence
+    const int unit = nb + lead;  // units of one group of this sequence
     const int g = (int)((t - seg_base) / unit);
-    const int64_t seg0 = seg_base + (int64_t)g * unit + kSegLead;  // its first tile
+    const int64_t seg0 = seg_base + (int64_t)g * unit + lead;  // its first tile
     const int ta = (int)((t > seg0 ? t : seg0) - seg0);
     const int te = (int)((t1 < seg0 + nb ? t1 : seg0 + nb) - seg0);
     if (te <= ta) break;  // the range ends inside this segment's lead-in units
     const bool complete = (ta == 0 && te == nb);
     // the range goes on into the next segment's tiles
-    const bool last_seg = !(te == nb && seg0 + nb + kSegLead < t1);
+    const bool last_seg = !(te == nb && seg0 + nb + lead < t1);
 
     // ---- this wave's tiles ----
     // Tiles go round-robin over the waves by their index in the workgroup's
@@ -630,7 +669,7 @@ struct CombineArgs {
   int32_t* lens;         // bumped when the decode appended
   int32_t* err_flag;     // nullable
   char* o;
-  int b, h, G, hg, m_cap, rec_floats, grid, min_tiles;
+  int b, h, G, hg, m_cap, rec_floats;
   int append;
 };
 
@@ -666,12 +705,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int bi = seg / a.G, g = seg % a.G;
   const int unit = a.prefix[bi + 1] - a.prefix[bi];  // lead-in units + tiles, or 0
   if (unit == 0) return;
-  const int nb = unit - kSegLead;
+  const int lead = a.prefix[a.b + 2];      // as the decode chose it
+  const int W = a.prefix[a.b + 3];
+  const int nb = unit - lead;
   const int64_t Tt = (int64_t)a.prefix[a.b] * a.G;
-  const int64_t segs = (int64_t)a.prefix[a.b + 1] * a.G;
-  const int W = effective_grid(Tt, segs, a.grid, a.min_tiles);
   const int64_t U0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * unit;  // first unit
-  const int64_t S0 = U0 + kSegLead;                                       // first tile
+  const int64_t S0 = U0 + lead;                                           // first tile
   const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
   // wf's range began in an earlier segment (whose last tile is unit U0 - 1)
@@ -730,10 +769,10 @@ size_t decode_record_bytes(int hg, int dh) {
   return f * sizeof(float);
 }
 
-// Schedule header: the [b + 1] tile prefix and the count of non-empty
-// sequences, padded to 256 bytes.
+// Schedule header: the [b + 1] units prefix, the count of non-empty
+// sequences, the lead-in and the effective grid, padded to 256 bytes.
 size_t decode_records_offset(int b) {
-  return (((size_t)b + 2) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return (((size_t)b + 4) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
 int decode_grid_cap(int b, int G, int m_cap) {
@@ -812,8 +851,6 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   ca.hg = a.hg;
   ca.m_cap = p.m_cap;
   ca.rec_floats = a.rec_floats;
-  ca.grid = grid;
-  ca.min_tiles = kDecodeWaves;
   ca.append = p.k_new != nullptr;
   constexpr int kHeadsPerBlock = 256 / (DH / 4);
   dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));

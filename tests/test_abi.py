@@ -90,7 +90,7 @@ def test_workspace_size_is_pure_host_arithmetic(lib):
     f = lib.mqa_decode_workspace_size
     c = cache(b=64, m_cap=8448, G=1, dh=128)
     n = f(32, ctypes.byref(c))
-    # schedule header (66 ints -> 512 B) + 2 * 2048 records of 32*130 floats
+    # schedule header (b + 4 = 68 ints -> 512 B) + 2 * 2048 records of 32*130 floats
     assert n == 512 + 2 * 2048 * (32 * 130 * 4)
     small = cache(b=1, m_cap=128, G=1, dh=64)
     assert f(4, ctypes.byref(small)) == 256 + 2 * 4 * ((4 * 66 + 3) // 4 * 4 * 4)

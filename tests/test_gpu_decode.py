@@ -89,6 +89,19 @@ def test_decode_many_sequences_multi_chunk_scan(append, fused):
     assert_parity(o, ref, torch.bfloat16, "b=600")
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_decode_many_long_sequences_lead_in_schedule(append):
+    """b > 64 with more tiles than one per wave of the grid: the schedule
+    with lead-in units across several 64-lane chunks (the step above has
+    fewer tiles, so it runs without lead-in)."""
+    announce(f"decode b=150 long append={append}")
+    cfg, inp = make(torch.bfloat16, 150, 16, 2, 64, 1000, 100, 900, seed=7110 + append)
+    assert int(((inp["lens"] + 31) // 32).sum()) * cfg.G > 8 * 256
+    o, _ = run_decode(inp, cfg.scale, append=append)
+    ref, _ = oracle_step(inp, cfg.scale, append=append)
+    assert_parity(o, ref, torch.bfloat16, "b=150 long")
+
+
 @pytest.mark.parametrize("window", [1, 7, 32, 33, 5000])
 def test_decode_local_window(window):
     """Local attention over the last `window` positions (current + 31 previous is 32)."""
