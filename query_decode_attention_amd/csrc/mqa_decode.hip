@@ -685,15 +685,15 @@ struct CombineArgs {
 // for it (every range of units holds a tile: the effective grid keeps ranges
 // longer than a lead-in): slot 1 for wf when its range began in an earlier
 // segment, slot 0 otherwise.
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+template <typename T, int DH, int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   constexpr int kD4 = DH / 4;            // float4 words per head row
-  constexpr int HPB = 256 / kD4;         // heads per block
+  constexpr int HPB = NT / kD4;          // heads per block
   constexpr int kBatch = 16;             // records per round trip
 
   if (a.append && blockIdx.x == 0 && blockIdx.y == 0) {
     int over = 0;
-    for (int bi = threadIdx.x; bi < a.b; bi += 256) {
+    for (int bi = threadIdx.x; bi < a.b; bi += NT) {
       const int raw = a.lens[bi];
       if (raw >= 0 && raw < a.m_cap) a.lens[bi] = raw + 1;
       else over = 1;
@@ -787,6 +787,10 @@ size_t decode_workspace_bytes(int b, int h, int G, int dh, int m_cap) {
 
 namespace {
 constexpr int kDecodeWaves = 8;
+// Threads per combine block: a block merges kCombineThreads / (d_h / 4)
+// heads of one segment.  Small blocks spread the records of a small step over
+// many CUs (a CU streams only ~20 GB/s).
+constexpr int kCombineThreads = 128;
 
 template <typename T, int DH>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
@@ -852,9 +856,10 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   ca.m_cap = p.m_cap;
   ca.rec_floats = a.rec_floats;
   ca.append = p.k_new != nullptr;
-  constexpr int kHeadsPerBlock = 256 / (DH / 4);
+  constexpr int kHeadsPerBlock = kCombineThreads / (DH / 4);
   dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));
-  hipLaunchKernelGGL((combine_kernel<T, DH>), cgrid, dim3(256), 0, s, ca);
+  hipLaunchKernelGGL((combine_kernel<T, DH, kCombineThreads>), cgrid, dim3(kCombineThreads), 0, s,
+                     ca);
   return hipGetLastError();
 }
 
