@@ -48,9 +48,9 @@ int check_cache_shape(const mqa_cache* c) {
   if (c->dtype != MQA_F32 && c->dtype != MQA_BF16) return MQA_ERR_DTYPE;
   if (c->d_h != 64 && c->d_h != 128) return MQA_ERR_DHEAD;
   if (c->b < 0 || c->m_cap < 1 || c->G < 1) return MQA_ERR_SHAPE;
-  // flat tile indices are 32-bit on the device
-  const int64_t tiles = (int64_t)c->b * c->G * ((c->m_cap + 31) / 32);
-  if (tiles >= ((int64_t)1 << 30)) return MQA_ERR_SHAPE;
+  // flat tile and schedule-unit indices are 32-bit on the device
+  const int64_t units = (int64_t)c->b * c->G * ((c->m_cap + 31) / 32 + mqa::kMaxSegLead);
+  if (units >= ((int64_t)1 << 30)) return MQA_ERR_SHAPE;
   return MQA_OK;
 }
 

@@ -144,6 +144,7 @@ __device__ __forceinline__ int tiles_of(const SeqView& s) {
 // CU streams only ~20 GB/s, and spreading the step over more CUs is worth
 // more than avoiding boundaries.
 constexpr int kSegLead = 6;
+static_assert(kSegLead <= kMaxSegLead, "lead-in within the unit-index bound");
 constexpr int kSmallUnits = 4;
 
 // Workgroups that share the Tv units of `segs` non-empty segments: the
@@ -187,6 +188,23 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Sum over the wave (uniform).
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// Maximum over the wave of non-negative values (uniform); the same moves as
+// wave_incl_scan, with max in place of +.
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // ------------------------------------------------------------ decode: tiles ----
 
 template <int NQ, bool FULL>
@@ -210,21 +228,25 @@ __device__ __forceinline__ void load_kv(const char* kp, const char* vp, bool val
   }
 }
 
+// This lane's chunks of the Q^T operand, read from LDS.
+template <int NQ>
+__device__ __forceinline__ void read_q(const u32x4 (*s_q)[64], int lane, u32x4 (&qr)[NQ]) {
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) qr[c] = s_q[c][lane];
+}
+
 // One decode tile: scores, online softmax with the tail masked at L, and P.V
 // with the V rows transposed in registers.
 template <typename T, int DH, bool FULL>
 __device__ __forceinline__ void tile_update(WaveState<TileShape<T, DH>::ND>& st,
                                             const u32x4 (&kr)[TileShape<T, DH>::NQ],
                                             const u32x4 (&vr)[TileShape<T, DH>::NQ],
-                                            const u32x4 (*s_q)[64], int lane,
+                                            const u32x4 (&qr)[TileShape<T, DH>::NQ],
                                             const SelOps<T>& sel, float scale_log2,
                                             int pos0, int L, int half) {
-  constexpr int NQ = TileShape<T, DH>::NQ;
   constexpr int ND = TileShape<T, DH>::ND;
+  constexpr int NQ = TileShape<T, DH>::NQ;
   constexpr int VTC = TileShape<T, DH>::VTC;
-  u32x4 qr[NQ];
-#pragma unroll
-  for (int c = 0; c < NQ; ++c) qr[c] = s_q[c][lane];
   const f32x16 s = tile_scores<T, NQ>(kr, qr);
   ProbTile<T> p;
   softmax_tile<T, ND, FULL>(st, s, scale_log2, pos0, L - 1, half, p);
@@ -293,29 +315,6 @@ __device__ __forceinline__ const char* q_row(const DecodeArgs& a, int bi, int g,
   return a.q + ((size_t)bi * a.h + (size_t)g * a.hg + qrow) * row_bytes;
 }
 
-// Every wave stages its share of the chunks through registers; the caller
-// barriers before the operand is read.
-template <typename T, int DH, int NW>
-__device__ __forceinline__ void stage_q(const DecodeArgs& a, u32x4 (*s_q)[64], int bi, int g,
-                                        int wave, int lane) {
-  constexpr int NQ = TileShape<T, DH>::NQ;
-  const int half = lane >> 5;
-  const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
-  for (int c = wave; c < NQ; c += NW) s_q[c][lane] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
-}
-
-// The same chunks as stage_q, copied straight into LDS (no registers, so the
-// copy can be in flight while the wave streams tiles); complete once this
-// wave's vmcnt reaches 0.
-template <typename T, int DH, int NW>
-__device__ __forceinline__ void copy_q(const DecodeArgs& a, u32x4 (*s_q)[64], int bi, int g,
-                                       int wave, int lane) {
-  constexpr int NQ = TileShape<T, DH>::NQ;
-  const int half = lane >> 5;
-  const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
-  for (int c = wave; c < NQ; c += NW) load_to_lds(qp + (2 * c + half) * 16, &s_q[c][0]);
-}
-
 // The whole Q^T operand copied by one wave into an LDS region of its own
 // (no other wave reads it, so no barrier is needed); complete once this
 // wave's vmcnt reaches 0.
@@ -336,14 +335,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
   constexpr int kWords = ND * 4 * 64;  // f32x4 words per slot
-  // Two Q^T buffers when they fit: the next segment's Q is fetched while the
-  // current one streams.
-  constexpr int kQBufs =
-      NW * sizeof(WaveSlot<ND>) + 2 * NQ * 64 * sizeof(u32x4) + 256 <= 160 * 1024 ? 2 : 1;
+  static_assert(kWords % (NW * 64) == 0, "every thread folds the same number of words");
   __shared__ WaveSlot<ND> s_slot[NW];
-  __shared__ u32x4 s_q[kQBufs][NQ][64];  // Q^T operand(s)
-  // In the first segment a wave reads Q^T from its own fold slot, which it
-  // does not need before it parks.
+  // A wave reads its piece's Q^T from its own fold slot, which it does not
+  // need before it parks.
   static_assert(NQ * 64 * sizeof(u32x4) <= sizeof(WaveSlot<ND>), "Q^T fits a fold slot");
 
   const int lane = threadIdx.x & 63;
@@ -376,12 +371,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const bool small = (int64_t)tiles * a.G <= (int64_t)NW * gridDim.x;
   const int lead = small ? 0 : kSegLead;
   const int total = tiles + lead * nonempty;                // units per group
-  const int64_t Tt = (int64_t)total * a.G;                  // units
-  const int64_t segs = (int64_t)nonempty * a.G;
+  // Unit indices fit in 32 bits: the cache shape check bounds
+  // b * G * (tiles per sequence + kMaxSegLead) below 2^30.
+  const int Tt = total * a.G;  // units
+  const int segs = nonempty * a.G;
   // Workgroups in use (see effective_grid): every wave has work, short
   // segments still run side by side.
   const int W = effective_grid(Tt, segs, gridDim.x, small ? kSmallUnits : NW, lead);
-  const int64_t t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
+  const int t0 = (int)wg_start(Tt, blockIdx.x, W), t1 = (int)wg_start(Tt, blockIdx.x + 1, W);
   // Units of the sequences of one chunk: their tiles plus `lead` per non-empty
   // sequence; u_excl / u_incl are prefixes within the chunk.
   auto chunk_units = [&](int v, int incl, int& u, int& u_incl) {
@@ -414,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // walk below reads lens from here, not from memory.
   int cbase = 0, craw = raw0;
   int b_cur = a.b;
-  int64_t seg_base = 0;
+  int seg_base = 0;
   if (t0 < t1) {
     int run = 0;
     for (int c = 0; c < a.b; c += 64) {
@@ -426,12 +423,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       int u, u_incl;
       chunk_units(v, incl, u, u_incl);
-      const int64_t lo = (int64_t)(run + u_incl - u) * a.G, hi = (int64_t)(run + u_incl) * a.G;
+      const int lo = (run + u_incl - u) * a.G, hi = (run + u_incl) * a.G;
       const uint64_t hit = __ballot(c + lane < a.b && u > 0 && lo <= t0 && t0 < hi);
       if (hit) {
         const int src = __builtin_ctzll(hit);
         b_cur = c + src;
-        seg_base = (int64_t)(run + __shfl(u_incl - u, src, 64)) * a.G;
+        seg_base = __builtin_amdgcn_readfirstlane((run + __shfl(u_incl - u, src, 64)) * a.G);
         cbase = c;
         craw = raw;
         break;
@@ -458,7 +455,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   SelOps<T> sel;
   sel.init(row, half);
   const size_t row_stride = (size_t)a.G * DH * sizeof(T);
-  int64_t t = t0;
   // lens entry of sequence bi (uniform), refilling the lane cache by chunks
   auto raw_of = [&](int bi) {
     if (bi < cbase || bi >= cbase + 64) {
@@ -467,197 +463,249 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     return __shfl(craw, bi - cbase, 64);
   };
-  // The segment after (bi, gi) in flat order, skipping empty sequences
-  // (bn == b: none).  Uniform.
-  auto next_seg = [&](int bi, int gi, int& bn, int& gn) {
-    bn = bi;
-    gn = gi + 1;
-    if (gn == a.G) {
-      gn = 0;
-      do {
-        ++bn;
-      } while (bn < a.b && tiles_of(seq_view_raw(a, raw_of(bn))) == 0);
-    }
-  };
-  int done = 0;           // tiles of this workgroup's range taken so far
-  int qb = 0;             // Q^T buffer of the current segment
-  bool q_staged = false;  // ... already copied during the previous segment
-  bool first = true;
 
+  // A piece is the part of one (sequence, group) segment inside this
+  // workgroup's range.  The waves are shared out over the pieces (up to NW of
+  // them per round; one round unless the range crosses more than NW
+  // segments), a piece's tiles go round-robin over its waves, and every wave
+  // streams one piece only.  So no wave waits for another before the one fold
+  // at the end of the round, and nothing is stored while tiles still stream
+  // (a wave's next loads would wait for those stores to complete).
+  int t = t0;
+  bool first_round = true;
   while (t < t1 && b_cur < a.b) {
-    const SeqView sv = seq_view_raw(a, raw_of(b_cur));
-    const int j0 = __builtin_amdgcn_readfirstlane(sv.j0);
-    const int L = __builtin_amdgcn_readfirstlane(sv.L);
-    const int app_pos = __builtin_amdgcn_readfirstlane(sv.app_pos);
-    const int nb = (L - j0 + kTileRows - 1) / kTileRows;
-    if (nb == 0) {
-      ++b_cur;
-      continue;
+    // ---- the pieces of this round; lane p describes piece p ----
+    int np = 0;
+    int p_b = 0, p_g = 0, p_raw = 0, p_ta = 0, p_te = 0, p_nb = 0;
+    while (np < NW && t < t1 && b_cur < a.b) {
+      const int raw = raw_of(b_cur);
+      const SeqView sv = seq_view_raw(a, raw);
+      const int nb = __builtin_amdgcn_readfirstlane((sv.L - sv.j0 + kTileRows - 1) / kTileRows);
+      if (nb == 0) {
+        ++b_cur;
+        continue;
+      }
+      const int unit = nb + lead;  // units of one group of this sequence
+      const int g = (t - seg_base) / unit;
+      const int seg0 = seg_base + g * unit + lead;  // its first tile
+      const int ta = (t > seg0 ? t : seg0) - seg0;
+      const int te = (t1 < seg0 + nb ? t1 : seg0 + nb) - seg0;
+      if (te <= ta) {  // the range ends inside this segment's lead-in units
+        t = t1;
+        break;
+      }
+      if (lane == np) {
+        p_b = b_cur;
+        p_g = g;
+        p_raw = raw;
+        p_ta = ta;
+        p_te = te;
+        p_nb = nb;
+      }
+      ++np;
+      t = seg0 + te;
+      if (g == a.G - 1 && te == nb) {
+        seg_base += a.G * unit;
+        ++b_cur;
+      }
     }
-    const int unit = nb + lead;  // units of one group of this sequence
-    const int g = (int)((t - seg_base) / unit);
-    const int64_t seg0 = seg_base + (int64_t)g * unit + lead;  // its first tile
-    const int ta = (int)((t > seg0 ? t : seg0) - seg0);
-    const int te = (int)((t1 < seg0 + nb ? t1 : seg0 + nb) - seg0);
-    if (te <= ta) break;  // the range ends inside this segment's lead-in units
-    const bool complete = (ta == 0 && te == nb);
-    // the range goes on into the next segment's tiles
-    const bool last_seg = !(te == nb && seg0 + nb + lead < t1);
+    if (np == 0) break;
+
+    // ---- waves per piece ----
+    // The smallest per-wave tile count k for which ceil(c_p / k) waves per
+    // piece fit in NW; the spare waves go to the piece with the most tiles
+    // (never more waves than tiles).  Piece p has waves [p_ws, p_ws + p_w).
+    const int c = lane < np ? p_te - p_ta : 0;
+    int p_w = 0, used = 0, p_ws = 0;
+    if (np == 1) {  // the usual case: one piece, min(c, NW) waves
+      const int c0 = __builtin_amdgcn_readfirstlane(c);
+      used = c0 < NW ? c0 : NW;
+      p_w = lane == 0 ? used : 0;
+    } else {
+      int k = (wave_sum(c) + NW - 1) / NW;
+      for (;;) {
+        p_w = (c + k - 1) / k;
+        used = wave_sum(p_w);
+        if (used <= NW) break;
+        ++k;
+      }
+      const int cmax = wave_max(c);
+      const int pbig = __builtin_ctzll(__ballot(lane < np && c == cmax));
+      const int room = __builtin_amdgcn_readlane(c - p_w, pbig);
+      const int give = NW - used < room ? NW - used : room;
+      if (lane == pbig) p_w += give;
+      used += give;
+      p_ws = wave_incl_scan(p_w) - p_w;
+    }
+    // this wave's piece, or -1 (more waves than tiles)
+    const int pw = wave < used ? __popcll(__ballot(lane < np && p_ws <= wave)) - 1 : -1;
+    // For the fold: bit w of `runs` is set where a run of waves (a piece, or
+    // the waves without one) starts; lane p of p_flags says whether piece p
+    // is a whole segment (bit 0) and which record slot it takes (bit 1).
+    int runs = used < NW ? 1 << used : 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x)
+      if (__ballot(lane < np && p_ws == x)) runs |= 1 << x;
+    const int p_flags =
+        ((p_ta == 0 && p_te == p_nb) ? 1 : 0) | ((first_round && lane == 0) ? 0 : 2);
 
     // ---- this wave's tiles ----
-    // Tiles go round-robin over the waves by their index in the workgroup's
-    // range (not in the segment), so a range that spans segments still gives
-    // every wave the same number of tiles, to within one.
-    const int rel0 = done;  // workgroup-relative index of tile ta
-    int tile = ta + ((wave - rel0) % NW + NW) % NW;
-    const size_t seq_off = ((size_t)b_cur * a.m_cap * a.G + (size_t)g) * DH * sizeof(T);
-    const size_t new_off = ((size_t)b_cur * a.G + (size_t)g) * DH * sizeof(T);
-    // Row of this lane in tile tl: pointers (the appended row comes from
-    // k_new / v_new) and whether it is visible.
-    auto row_ptrs = [&](int tl, const char*& kp, const char*& vp) {
-      const int pos = j0 + tl * kTileRows + row;
-      const bool is_new = (pos == app_pos);
-      kp = is_new ? a.k_new + new_off : a.k + seq_off + (size_t)pos * row_stride;
-      vp = is_new ? a.v_new + new_off : a.v + seq_off + (size_t)pos * row_stride;
-      return pos < L;
-    };
-    // The concat: the lane holding the appended row stores it into the cache.
-    auto store_new_row = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
-      const int pos = j0 + tl * kTileRows + row;
-      if (pos != app_pos) return;
-      char* kc = a.k + seq_off + (size_t)pos * row_stride;
-      char* vc = a.v + seq_off + (size_t)pos * row_stride;
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        *reinterpret_cast<u32x4*>(kc + (2 * c + half) * 16) = kr[c];
-        *reinterpret_cast<u32x4*>(vc + (2 * c + half) * 16) = vr[c];
-      }
-    };
-    const u32x4 (*qsrc)[64] = s_q[qb];  // Q^T operand of this segment
-    bool own = false;                    // ... in this wave's own slot
     WaveState<ND> st;
     st.reset();
-    auto update = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
-      const int pos0 = j0 + tl * kTileRows;
-      if (pos0 + kTileRows <= L)
-        tile_update<T, DH, true>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
-      else
-        tile_update<T, DH, false>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
-    };
-
-    // ---- Q^T of this segment, and the copy of the next one's ----
-    // First segment: every wave with tiles copies the whole operand into its
-    // own fold slot, so no wave waits for another and the copy shares its
-    // round trip with the wave's first tile.  Later segments: the operand was
-    // copied during the previous segment, or (one buffer) all waves stage it
-    // now.
-    if (first) {
-      qsrc = own_q;
-      if (tile < te) {
-        copy_q_own<T, DH>(a, own_q, b_cur, g, lane);
-        own = true;
-      }
-    } else if (!q_staged) {
-      stage_q<T, DH, NW>(a, s_q[qb], b_cur, g, wave, lane);
-      __syncthreads();
-    }
-    // When the range goes on, the next segment's Q^T is copied into the
-    // other buffer now and lands while this segment streams.
-    bool next_staged = false;
-    if constexpr (kQBufs == 2) {
-      if (!last_seg) {
-        int bn, gn;
-        next_seg(b_cur, g, bn, gn);
-        copy_q<T, DH, NW>(a, s_q[qb ^ 1], bn, gn, wave, lane);
-        next_staged = true;
-      }
-    }
-
-    // The Q^T copies issued above must land before this wave reads its own
-    // copy, before the barriers below publish the next segment's, and before
-    // the wave parks over its own.  The wait is taken with the first tile,
-    // whose loads it needs anyway, so it never covers the appended row's
-    // stores (waiting on those would hold up the fold).
-    bool dma_wait = next_staged || own;
-    for (; tile < te; tile += NW) {
-      const int pos0 = j0 + tile * kTileRows;
-      u32x4 kr[NQ], vr[NQ];
-      if (pos0 + kTileRows <= L && app_pos < pos0) {
-        const size_t off = seq_off + (size_t)(pos0 + row) * row_stride;
-        load_kv<NQ, true>(a.k + off, a.v + off, true, half, kr, vr);
-        if (dma_wait) {
-          __builtin_amdgcn_s_waitcnt(0x0F70);
-          dma_wait = false;
+    if (pw >= 0) {
+      const int bi = __builtin_amdgcn_readlane(p_b, pw);
+      const int g = __builtin_amdgcn_readlane(p_g, pw);
+      const int te = __builtin_amdgcn_readlane(p_te, pw);
+      const int step = __builtin_amdgcn_readlane(p_w, pw);
+      const SeqView sv = seq_view_raw(a, __builtin_amdgcn_readlane(p_raw, pw));
+      const int j0 = __builtin_amdgcn_readfirstlane(sv.j0);
+      const int L = __builtin_amdgcn_readfirstlane(sv.L);
+      const int app_pos = __builtin_amdgcn_readfirstlane(sv.app_pos);
+      const size_t seq_off = ((size_t)bi * a.m_cap * a.G + (size_t)g) * DH * sizeof(T);
+      const size_t new_off = ((size_t)bi * a.G + (size_t)g) * DH * sizeof(T);
+      // Row of this lane in tile tl: pointers (the appended row comes from
+      // k_new / v_new) and whether it is visible.
+      auto row_ptrs = [&](int tl, const char*& kp, const char*& vp) {
+        const int pos = j0 + tl * kTileRows + row;
+        const bool is_new = (pos == app_pos);
+        kp = is_new ? a.k_new + new_off : a.k + seq_off + (size_t)pos * row_stride;
+        vp = is_new ? a.v_new + new_off : a.v + seq_off + (size_t)pos * row_stride;
+        return pos < L;
+      };
+      // The concat: the lane holding the appended row stores it into the
+      // cache (in the segment's last tile, so no later load waits for it).
+      auto store_new_row = [&](int tl, const u32x4 (&kr)[NQ], const u32x4 (&vr)[NQ]) {
+        const int pos = j0 + tl * kTileRows + row;
+        if (pos != app_pos) return;
+        char* kc = a.k + seq_off + (size_t)pos * row_stride;
+        char* vc = a.v + seq_off + (size_t)pos * row_stride;
+#pragma unroll
+        for (int cc = 0; cc < NQ; ++cc) {
+          *reinterpret_cast<u32x4*>(kc + (2 * cc + half) * 16) = kr[cc];
+          *reinterpret_cast<u32x4*>(vc + (2 * cc + half) * 16) = vr[cc];
         }
-        tile_update<T, DH, true>(st, kr, vr, qsrc, lane, sel, a.scale_log2, pos0, L, half);
-      } else {
-        // last tile of the segment: ragged, and/or holding the appended row
+      };
+
+      // Q^T of the piece into this wave's own fold slot; the copy shares its
+      // memory round trip with the first tile, whose wait covers it.
+      copy_q_own<T, DH>(a, own_q, bi, g, lane);
+      const uint32_t lane_off = (uint32_t)row * (uint32_t)row_stride;
+      // Every tile of the piece is whole and free of the appended row except
+      // perhaps the segment's last one (ragged, and/or holding the appended
+      // row); that one is taken after the loop by the wave it falls to.
+      const int nb = __builtin_amdgcn_readlane(p_nb, pw);
+      const int last0 = j0 + (nb - 1) * kTileRows;
+      const bool special = te == nb && (last0 + kTileRows > L || app_pos >= last0);
+      const int te_whole = special ? te - 1 : te;
+      int tile = __builtin_amdgcn_readlane(p_ta, pw) + (wave - __builtin_amdgcn_readlane(p_ws, pw));
+      // The Q^T copy lands with the wave's first tile, which waits for both;
+      // from the second tile on, the Q^T reads from LDS are issued right
+      // behind the tile's loads and complete while those are in flight.
+      auto whole_tile = [&](bool first_tile) {
+        const int pos0 = j0 + tile * kTileRows;
+        u32x4 kr[NQ], vr[NQ], qr[NQ];
+        // uniform base of the tile plus a 32-bit offset per lane
+        const size_t base = seq_off + (size_t)pos0 * row_stride;
+        load_kv<NQ, true>(a.k + base + lane_off, a.v + base + lane_off, true, half, kr, vr);
+        if (first_tile) __builtin_amdgcn_s_waitcnt(0x0F70);
+        read_q<NQ>(own_q, lane, qr);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_update<T, DH, true>(st, kr, vr, qr, sel, a.scale_log2, pos0, L, half);
+      };
+      bool q_landed = false;
+      if (tile < te_whole) {
+        whole_tile(true);
+        q_landed = true;
+        for (tile += step; tile < te_whole; tile += step) whole_tile(false);
+      }
+      if (special && tile == te - 1) {
+        u32x4 kr[NQ], vr[NQ], qr[NQ];
         const char *kp, *vp;
         const bool valid = row_ptrs(tile, kp, vp);
         load_kv<NQ, false>(kp, vp, valid, half, kr, vr);
-        if (dma_wait) {
-          __builtin_amdgcn_s_waitcnt(0x0F70);
-          dma_wait = false;
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        q_landed = true;
         store_new_row(tile, kr, vr);
-        update(tile, kr, vr);
+        read_q<NQ>(own_q, lane, qr);
+        // masked at L (a whole tile passes the mask unchanged)
+        tile_update<T, DH, false>(st, kr, vr, qr, sel, a.scale_log2, j0 + tile * kTileRows, L,
+                                  half);
       }
+      if (!q_landed) __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile: the copy still lands
     }
-    // a wave without tiles here still has its copy of the next Q^T in flight
-    if (dma_wait) __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // ---- fold the waves: park in LDS, combine in a fixed order ----
+    // ---- fold: park in LDS, combine each run of waves in a fixed order ----
     park<ND>(st, s_slot[wave], lane);
     __syncthreads();
-    // Thread t folds the f32x4 words t, t + NW*64, ... of the slots; all of
-    // them belong to head t % 32, whose max, weights and sum it derives
-    // itself (no separate per-head pass, no extra barrier).
     {
+      // Thread t folds the f32x4 words t, t + NW*64, ... of the slots; all of
+      // them belong to head t % 32, whose per-run max, weights and sum it
+      // derives itself.
       const int hd = threadIdx.x & 31;
-      float M = kNegInf;
+      float m[NW], f[NW], M[NW], Ls[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_slot[w].m[hd]);
-      const float Ms = (M == kNegInf) ? 0.f : M;
-      float f[NW];
-      float l = 0.f;
+      for (int x = 0; x < NW; ++x) m[x] = s_slot[x].m[hd];
+      float run = kNegInf;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        f[w] = fast_exp2(s_slot[w].m[hd] - Ms);
-        l += (s_slot[w].l[hd] + s_slot[w].l[hd + 32]) * f[w];
+      for (int x = 0; x < NW; ++x) {
+        if (runs >> x & 1) run = kNegInf;
+        run = fmaxf(run, m[x]);
+        M[x] = run;
       }
-      float* rec = a.records + ((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * a.rec_floats;
-      if (hd < a.hg) {
-        for (int e = threadIdx.x; e < kWords; e += NW * 64) {
-          const SlotIndex ix(e);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int w = 0; w < NW; ++w) acc += s_slot[w].o[ix.blk][ix.r4][ix.lane] * f[w];
-          if (complete) {
-            const float inv = 1.0f / l;
-            T* op = reinterpret_cast<T*>(a.o) + ((size_t)b_cur * a.h + (size_t)g * a.hg + hd) * DH +
-                    ix.d();
-            store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-          } else {
-            *reinterpret_cast<f32x4*>(rec + (size_t)hd * DH + ix.d()) = acc;
-            if (e < 32) {
-              rec[(size_t)a.hg * DH + hd] = M;
-              rec[(size_t)a.hg * DH + a.hg + hd] = l;
+      for (int x = NW - 2; x >= 0; --x)
+        if (!(runs >> (x + 1) & 1)) M[x] = M[x + 1];
+      float sum = 0.f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) {
+        f[x] = fast_exp2(m[x] - (M[x] == kNegInf ? 0.f : M[x]));
+        if (runs >> x & 1) sum = 0.f;
+        sum += (s_slot[x].l[hd] + s_slot[x].l[hd + 32]) * f[x];
+        Ls[x] = sum;
+      }
+#pragma unroll
+      for (int x = NW - 2; x >= 0; --x)
+        if (!(runs >> (x + 1) & 1)) Ls[x] = Ls[x + 1];
+      // Every thread runs the loop (the piece descriptors are read across
+      // lanes with readlane, which needs all lanes active); only heads below
+      // h/G store.
+      const bool real_head = hd < a.hg;
+#pragma unroll
+      for (int kw = 0; kw < kWords / (NW * 64); ++kw) {
+        const int e = threadIdx.x + kw * NW * 64;
+        const SlotIndex ix(e);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x = 0; x < NW; ++x) {
+          if (runs >> x & 1) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc += s_slot[x].o[ix.blk][ix.r4][ix.lane] * f[x];
+          const bool run_end = (x == NW - 1) || (runs >> (x + 1) & 1);
+          if (run_end && x < used) {
+            const int pp = __popc((unsigned)runs & ((2u << x) - 1)) - 1;  // its piece
+            const int bi = __builtin_amdgcn_readlane(p_b, pp);
+            const int g = __builtin_amdgcn_readlane(p_g, pp);
+            const int flags = __builtin_amdgcn_readlane(p_flags, pp);
+            if (real_head) {
+              if (flags & 1) {  // the whole segment: normalised output
+                const float inv = 1.0f / Ls[x];
+                T* op = reinterpret_cast<T*>(a.o) +
+                        ((size_t)bi * a.h + (size_t)g * a.hg + hd) * DH + ix.d();
+                store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+              } else {  // a partial record for the combine
+                float* rec = a.records + ((size_t)blockIdx.x * 2 + (flags >> 1)) * a.rec_floats;
+                *reinterpret_cast<f32x4*>(rec + (size_t)hd * DH + ix.d()) = acc;
+                if (e < 32) {
+                  rec[(size_t)a.hg * DH + hd] = M[x];
+                  rec[(size_t)a.hg * DH + a.hg + hd] = Ls[x];
+                }
+              }
             }
           }
         }
       }
     }
-    __syncthreads();  // LDS slots are reused by the next segment
-
-    if (next_staged) qb ^= 1;
-    q_staged = next_staged;
-    first = false;
-    done += te - ta;
-    t = seg0 + te;
-    if (g == a.G - 1 && te == nb) {
-      seg_base += (int64_t)a.G * unit;
-      ++b_cur;
-    }
+    first_round = false;
+    if (t < t1 && b_cur < a.b) __syncthreads();  // the slots are reused
   }
 }
 

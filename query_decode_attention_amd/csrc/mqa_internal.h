@@ -10,6 +10,10 @@ namespace mqa {
 
 // Largest split-K grid the decode may use; bounds the workspace.
 constexpr int kMaxDecodeGrid = 2048;
+// Upper bound of the decode schedule's lead-in units per segment; the cache
+// shape check keeps b * G * (tiles per sequence + kMaxSegLead) below 2^30,
+// so unit indices fit in 32 bits on the device.
+constexpr int kMaxSegLead = 8;
 // Cache positions per wave tile in the decode and prefill kernels.
 constexpr int kTileRows = 32;
 
