@@ -642,9 +642,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       // them belong to head t % 32, whose per-run max, weights and sum it
       // derives itself.
       const int hd = threadIdx.x & 31;
-      float m[NW], f[NW], M[NW], Ls[NW];
+      constexpr int KW = kWords / (NW * 64);  // words per thread
+      // Every LDS read of the fold is issued up front, ahead of the scans and
+      // the (scalar) branches of the stores, so that their latencies overlap.
+      float m[NW], l0[NW], l1[NW], f[NW], M[NW], Ls[NW];
+      f32x4 wd[KW][NW];
 #pragma unroll
-      for (int x = 0; x < NW; ++x) m[x] = s_slot[x].m[hd];
+      for (int x = 0; x < NW; ++x) {
+        m[x] = s_slot[x].m[hd];
+        l0[x] = s_slot[x].l[hd];
+        l1[x] = s_slot[x].l[hd + 32];
+      }
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) {
+        const SlotIndex ix(threadIdx.x + kw * NW * 64);
+#pragma unroll
+        for (int x = 0; x < NW; ++x) wd[kw][x] = s_slot[x].o[ix.blk][ix.r4][ix.lane];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float run = kNegInf;
 #pragma unroll
       for (int x = 0; x < NW; ++x) {
@@ -660,7 +675,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       for (int x = 0; x < NW; ++x) {
         f[x] = fast_exp2(m[x] - (M[x] == kNegInf ? 0.f : M[x]));
         if (runs >> x & 1) sum = 0.f;
-        sum += (s_slot[x].l[hd] + s_slot[x].l[hd + 32]) * f[x];
+        sum += (l0[x] + l1[x]) * f[x];
         Ls[x] = sum;
       }
 #pragma unroll
@@ -671,14 +686,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       // h/G store.
       const bool real_head = hd < a.hg;
 #pragma unroll
-      for (int kw = 0; kw < kWords / (NW * 64); ++kw) {
+      for (int kw = 0; kw < KW; ++kw) {
         const int e = threadIdx.x + kw * NW * 64;
         const SlotIndex ix(e);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < NW; ++x) {
           if (runs >> x & 1) acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          acc += s_slot[x].o[ix.blk][ix.r4][ix.lane] * f[x];
+          acc += wd[kw][x] * f[x];
           const bool run_end = (x == NW - 1) || (runs >> (x + 1) & 1);
           if (run_end && x < used) {
             const int pp = __popc((unsigned)runs & ((2u << x) - 1)) - 1;  // its piece
