@@ -14,29 +14,33 @@
 // segment are cut into tiles of 32.  All segments form one flat list of U
 // units -- a few lead-in units, then the segment's tiles -- and workgroup
 // w of a grid of W takes units [U*w/W, U*(w+1)/W): every workgroup streams
-// about the same number of bytes whatever the length mix, a few tiles fewer
-// for each segment boundary its range crosses (see kSegLead).  Each
-// wave derives this schedule from lens by itself (a DPP prefix sum over the
+// about the same number of bytes whatever the length mix (a few tiles fewer
+// for each segment boundary its range crosses, see kSegLead).  Each wave
+// derives this schedule from lens by itself (a DPP prefix sum over the
 // wave) and keeps the lens entries it needs in registers, so the schedule
 // costs no host synchronisation, no barrier and one read of lens.
 //
-// Q.  A segment's Q^T operand sits in LDS for all its tiles.  In a
-// workgroup's first segment every wave copies it into its own fold slot (free
-// until that wave parks), so the copy shares a round trip with the wave's
-// first tile and no wave waits for another.  When a workgroup's range goes
-// on past the current segment, the next segment's Q^T is copied into a shared
-// LDS buffer while the current one streams, so the switch to it costs no
-// memory round trip.
+// Pieces.  The part of a segment inside a workgroup's range is a piece.  The
+// NW waves are shared out over the range's pieces, a piece's tiles go
+// round-robin over its waves, and every wave streams one piece only: no wave
+// waits for another until the range is done, and no partial result is
+// stored while tiles still stream (on gfx9 a wave's next loads wait, in
+// order, for the stores it issued before them, and under a read-saturated
+// HBM a store takes microseconds to complete).  At the end all waves park
+// their (max, sum, accumulator) in LDS and the workgroup folds the waves of
+// each piece in a fixed order.  A segment that one workgroup covers
+// completely is normalised and written; a piece of a segment shared with
+// neighbouring workgroups becomes an fp32 partial record that the combine
+// kernel merges.  The records cross from one workgroup to another only
+// through the kernel boundary: publishing them inside the kernel would need
+// an agent-scope release per workgroup, i.e. a write-back of an XCD's whole
+// L2, which costs far more on gfx950 than a second small launch.
 //
-// Inside a workgroup, wave k takes every NW-th tile of a segment.  At the end
-// of a segment all waves park their (max, sum, accumulator) in LDS and the
-// workgroup folds them in a fixed order.  A segment that one workgroup covers
-// completely is normalised and written; a segment shared with neighbouring
-// workgroups becomes an fp32 partial record that the combine kernel merges.
-// The records cross from one workgroup to another only through the kernel
-// boundary: publishing them inside the kernel would need an agent-scope
-// release per workgroup, i.e. a write-back of an XCD's whole L2, which costs
-// far more on gfx950 than a second small launch.
+// Q.  Every wave copies its piece's Q^T operand with the direct-to-LDS load
+// into its own fold slot (free until the wave parks); the copy shares a
+// memory round trip with the wave's first tile, and no wave waits for
+// another.  From the second tile on, the Q^T reads from LDS are issued right
+// behind the tile's loads.
 //
 // Fused append.  With k_new/v_new, sequence b attends over L_old + 1
 // positions; the row at L_old is read from k_new/v_new (never from the cache)
@@ -136,9 +140,11 @@ __device__ __forceinline__ int tiles_of(const SeqView& s) {
 // Schedule units.  Every non-empty segment is `lead` virtual units (no
 // positions) followed by its tiles, and workgroups split the units evenly.  A
 // workgroup whose range reaches into a further segment thereby takes about
-// `lead` fewer tiles, which pays for the fold at the segment boundary (the
-// waves of a workgroup meet there, so its critical path grows by about half
-// a round of tiles per boundary crossed).  A small step (at most one tile per
+// `lead` fewer tiles, which pays for what a boundary costs it: its waves
+// are split between two pieces (whole waves, so some take a tile more than
+// an even split would give them), a second Q^T copy and a second record.
+// (c3 kernel for lead-ins 0, 1, 2, 4, 6: 32.5, 32.1, 31.7, 31.5, 31.4 us.)
+// A small step (at most one tile per
 // wave of the launched grid) has no lead-in and up to one workgroup per
 // kSmallUnits units: there every workgroup has about one round of loads, a
 // CU streams only ~20 GB/s, and spreading the step over more CUs is worth
