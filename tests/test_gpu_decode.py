@@ -102,6 +102,29 @@ def test_decode_many_long_sequences_lead_in_schedule(append):
     assert_parity(o, ref, torch.bfloat16, "b=150 long")
 
 
+@pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
+def test_decode_short_sequences_several_rounds(append, fused):
+    """More segments than 8 per workgroup of the largest grid (256): some
+    workgroup ranges cross more than NW = 8 segments, so they are streamed
+    and folded in several rounds of at most 8 pieces."""
+    announce(f"decode b=4096 short append={append} fused={fused}")
+    cfg, inp = make(torch.bfloat16, 4096, 8, 1, 64, 64, 1, 40, seed=7300 + append)
+    assert cfg.b * cfg.G > 8 * 256
+    o, _ = run_decode(inp, cfg.scale, append=append, fused=fused)
+    ref, _ = oracle_step(inp, cfg.scale, append=append)
+    assert_parity(o, ref, torch.bfloat16, "b=4096 short")
+
+
+def test_decode_short_sequences_several_rounds_gqa_d128():
+    """The same with G = 2 groups of 8 heads, d_h = 128 and fp32 inputs."""
+    announce("decode b=1500 G=2 fp32 short")
+    cfg, inp = make(torch.float32, 1500, 16, 2, 128, 48, 0, 47, seed=7310)
+    assert cfg.b * cfg.G > 8 * 256
+    o, _ = run_decode(inp, cfg.scale, append=True)
+    ref, _ = oracle_step(inp, cfg.scale, append=True)
+    assert_parity(o, ref, torch.float32, "b=1500 G=2 fp32 short")
+
+
 @pytest.mark.parametrize("window", [1, 7, 32, 33, 5000])
 def test_decode_local_window(window):
     """Local attention over the last `window` positions (current + 31 previous is 32)."""
