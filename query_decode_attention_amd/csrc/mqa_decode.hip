@@ -392,26 +392,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     u = v > 0 ? v + lead : 0;
     u_incl = incl + lead * (lanes_below(ne) + (v > 0 ? 1 : 0));
   };
-  if (blockIdx.x == 0 && wave == 0) {  // the units prefix, for the combine
-    int run = 0;
-    for (int c = 0; c < a.b; c += 64) {
-      int v = v0, incl = incl0;
-      if (c > 0) {
-        v = (c + lane < a.b) ? tiles_of(seq_view(a, c + lane)) : 0;
-        incl = wave_incl_scan(v);
-      }
-      int u, u_incl;
-      chunk_units(v, incl, u, u_incl);
-      if (c + lane < a.b) a.prefix[c + lane] = run + u_incl - u;
-      run += __shfl(u_incl, 63, 64);
-    }
-    if (lane == 0) {
-      a.prefix[a.b] = total;
-      a.prefix[a.b + 1] = nonempty;
-      a.prefix[a.b + 2] = lead;
-      a.prefix[a.b + 3] = W;
-    }
-  }
 
   // lens entries of sequences cbase .. cbase + 63, one per lane: the segment
   // walk below reads lens from here, not from memory.
@@ -444,19 +424,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     b_cur = __builtin_amdgcn_readfirstlane(b_cur);
   }
 
-  // Sequences with nothing visible get zeros; wave k of workgroup 0 checks
-  // sequences k*64 .. k*64+63, NW*64 at a time, and writes their rows.
-  if (blockIdx.x == 0) {
-    for (int c = wave * 64; c < a.b; c += NW * 64) {
-      uint64_t empty = __ballot(c + lane < a.b && tiles_of(seq_view(a, c + lane)) == 0);
-      while (empty) {
-        const int bi = c + __builtin_ctzll(empty);
-        empty &= empty - 1;
-        T* op = reinterpret_cast<T*>(a.o) + (size_t)bi * a.h * DH;
-        for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  }
 
   SelOps<T> sel;
   sel.init(row, half);
@@ -595,7 +562,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       // Q^T of the piece into this wave's own fold slot; the copy shares its
       // memory round trip with the first tile, whose wait covers it.
       copy_q_own<T, DH>(a, own_q, bi, g, lane);
-      const uint32_t lane_off = (uint32_t)row * (uint32_t)row_stride;
+      // this lane's byte offset in a tile (row, 16-byte half), so that a
+      // tile load is a uniform base plus one 32-bit offset per lane
+      const uint32_t lane_off = (uint32_t)row * (uint32_t)row_stride + (uint32_t)half * 16u;
       // Every tile of the piece is whole and free of the appended row except
       // perhaps the segment's last one (ragged, and/or holding the appended
       // row); that one is taken after the loop by the wave it falls to.
@@ -612,7 +581,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         u32x4 kr[NQ], vr[NQ], qr[NQ];
         // uniform base of the tile plus a 32-bit offset per lane
         const size_t base = seq_off + (size_t)pos0 * row_stride;
-        load_kv<NQ, true>(a.k + base + lane_off, a.v + base + lane_off, true, half, kr, vr);
+        load_kv<NQ, true>(a.k + base + lane_off, a.v + base + lane_off, true, 0, kr, vr);
         if (first_tile) __builtin_amdgcn_s_waitcnt(0x0F70);
         read_q<NQ>(own_q, lane, qr);
         __builtin_amdgcn_sched_barrier(0);
@@ -727,6 +696,45 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     first_round = false;
     if (t < t1 && b_cur < a.b) __syncthreads();  // the slots are reused
+  }
+
+  // Workgroup 0 writes the schedule header for the combine and zeros the rows
+  // of sequences with nothing visible.  Both are stores; they come after the
+  // streaming, because a wave's loads wait for the stores it issued earlier.
+  if (blockIdx.x == 0 && wave == 0) {  // the units prefix, for the combine
+    int run = 0;
+    for (int c = 0; c < a.b; c += 64) {
+      int v = v0, incl = incl0;
+      if (c > 0) {
+        v = (c + lane < a.b) ? tiles_of(seq_view(a, c + lane)) : 0;
+        incl = wave_incl_scan(v);
+      }
+      int u, u_incl;
+      chunk_units(v, incl, u, u_incl);
+      if (c + lane < a.b) a.prefix[c + lane] = run + u_incl - u;
+      run += __shfl(u_incl, 63, 64);
+    }
+    if (lane == 0) {
+      a.prefix[a.b] = total;
+      a.prefix[a.b + 1] = nonempty;
+      a.prefix[a.b + 2] = lead;
+      a.prefix[a.b + 3] = W;
+    }
+  }
+
+  // Sequences with nothing visible get zeros; wave k of workgroup 0 checks
+  // sequences k*64 .. k*64+63, NW*64 at a time, and writes their rows.
+  if (blockIdx.x == 0) {
+    for (int c = wave * 64; c < a.b; c += NW * 64) {
+      const int raw = c == 0 ? raw0 : (c + lane < a.b ? a.lens[c + lane] : 0);
+      uint64_t empty = __ballot(c + lane < a.b && tiles_of(seq_view_raw(a, raw)) == 0);
+      while (empty) {
+        const int bi = c + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        T* op = reinterpret_cast<T*>(a.o) + (size_t)bi * a.h * DH;
+        for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
+      }
+    }
   }
 }
 
