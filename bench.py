@@ -487,7 +487,7 @@ def main():
                     help="append with mqa_kv_append, then mqa_decode (two launches per step)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
                     help="also run 3 plain device copies of MB MiB (calibrates profiler byte counters)")
-    ap.add_argument("--only", choices=["c2", "c4", "c5", "encdec", "beam4"],
+    ap.add_argument("--only", choices=["c2", "c4", "c5", "encdec", "beam4", "paper"],
                     help="run just this secondary workload and print its numbers (for profiling "
                          "one workload alone); no headline line")
     args = ap.parse_args()
@@ -526,6 +526,8 @@ def main():
             "c5": lambda: prefill_result(W.C5, steps or 10, torch, mqa),
             "encdec": lambda: attend_result(W.ENCDEC, steps or 10, torch, mqa),
             "beam4": lambda: beam_result(W.BEAM4, steps or 96, torch, mqa),
+            "paper": lambda: decode_result(DecodeBench(W.PAPER_MQA, 8, torch, mqa), steps or 320,
+                                           32, use_graph),
         }[args.only]
         r = run()
         print(json.dumps({"only": args.only, **{k: (round(v, 4) if isinstance(v, float) else v)
@@ -566,6 +568,15 @@ def main():
         extra["c2_mha_b8_m2048"] = {k: round(v, 4) for k, v in c2m.items()}
         extra["mha_over_mqa_time_ratio"] = round(c2m["ms_per_step"] / c2["ms_per_step"], 2)
         log(f"MHA/MQA time ratio {extra['mha_over_mqa_time_ratio']}")
+        log("the pages' speed setting: b=1024, h=8, d_h=128, 128 positions, MQA vs MHA")
+        pq = decode_result(DecodeBench(W.PAPER_MQA, 8, torch, mqa), 320, 32, use_graph)
+        torch.cuda.empty_cache()
+        ph = decode_result(DecodeBench(W.PAPER_MHA, 4, torch, mqa), 160, 8, use_graph)
+        torch.cuda.empty_cache()
+        extra["paper_mqa_b1024_h8_m128"] = {k: round(v, 4) for k, v in pq.items()}
+        extra["paper_mha_b1024_h8_m128"] = {k: round(v, 4) for k, v in ph.items()}
+        extra["paper_mha_over_mqa_time_ratio"] = round(ph["ms_per_step"] / pq["ms_per_step"], 2)
+        log(f"paper setting MHA/MQA time ratio {extra['paper_mha_over_mqa_time_ratio']}")
         log("c4 GQA long context")
         c4 = decode_result(DecodeBench(W.C4, 1, torch, mqa), 30, 3, use_graph)
         torch.cuda.empty_cache()

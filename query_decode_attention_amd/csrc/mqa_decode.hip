@@ -353,24 +353,58 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   u32x4 (*const own_q)[64] = reinterpret_cast<u32x4 (*)[64]>(&s_slot[wave]);
 
   // ---- schedule (each wave on its own) ----
+  // lens is read kLensRegs chunks of 64 entries at a time with all loads in
+  // flight together (one memory round trip per 1024 sequences, not one per
+  // 64); when b <= 64 * kLensRegs the entries stay in registers for the
+  // search below.
+  constexpr int kLensRegs = 16;
+  const int nchunks = (a.b + 63) / 64;
+  const bool lens_in_regs = nchunks <= kLensRegs;
+  int rawr[kLensRegs];
+  auto load_chunks = [&](int g0) {
+    // unconditional loads of clamped indices (no branch between them, so they
+    // are all in flight together); entries past b read as 0
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      const int i = (g0 + k) * 64 + lane;
+      if (g0 + k < nchunks)
+        rawr[k] = a.lens[i < a.b ? i : a.b - 1];
+      else
+        rawr[k] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k)
+      if ((g0 + k) * 64 + lane >= a.b) rawr[k] = 0;
+  };
   // Pass 1: tiles of every sequence (per group) and the non-empty count,
   // which fix the lead-in.  raw0 / v0 / incl0: lens entry, tiles and their
   // inclusive prefix for sequence `lane` (the first 64), reused below.
   int tiles = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
-  for (int c = 0; c < a.b; c += 64) {
-    int raw = 0, v = 0;
-    if (c + lane < a.b) {
-      raw = a.lens[c + lane];
-      v = tiles_of(seq_view_raw(a, raw));
+  if (nchunks == 1) {  // b <= 64: one chunk, a compact path
+    raw0 = lane < a.b ? a.lens[lane] : 0;
+    v0 = lane < a.b ? tiles_of(seq_view_raw(a, raw0)) : 0;
+    incl0 = wave_incl_scan(v0);
+    tiles = __builtin_amdgcn_readlane(incl0, 63);
+    nonempty = __popcll(__ballot(v0 > 0));
+  }
+  if (__builtin_expect(nchunks > 1, 0)) {
+  for (int g0 = 0; g0 < nchunks; g0 += kLensRegs) {
+    load_chunks(g0);
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      if (g0 + k >= nchunks) break;
+      const int c = (g0 + k) * 64;
+      const int v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, rawr[k])) : 0;
+      const int incl = wave_incl_scan(v);
+      if (c == 0) {
+        raw0 = rawr[k];
+        v0 = v;
+        incl0 = incl;
+      }
+      tiles += __builtin_amdgcn_readlane(incl, 63);
+      nonempty += __popcll(__ballot(v > 0));
     }
-    const int incl = wave_incl_scan(v);
-    if (c == 0) {
-      raw0 = raw;
-      v0 = v;
-      incl0 = incl;
-    }
-    tiles += __shfl(incl, 63, 64);
-    nonempty += __popcll(__ballot(v > 0));
+  }
   }
   tiles = __builtin_amdgcn_readfirstlane(tiles);
   nonempty = __builtin_amdgcn_readfirstlane(nonempty);
@@ -398,28 +432,45 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   int cbase = 0, craw = raw0;
   int b_cur = a.b;
   int seg_base = 0;
-  if (t0 < t1) {
+  if (t0 < t1 && nchunks == 1) {
+    int u, u_incl;
+    chunk_units(v0, incl0, u, u_incl);
+    const uint64_t hit = __ballot(lane < a.b && u > 0 && (u_incl - u) * a.G <= t0 && t0 < u_incl * a.G);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      b_cur = __builtin_amdgcn_readfirstlane(src);
+      seg_base = __builtin_amdgcn_readfirstlane(__shfl(u_incl - u, src, 64) * a.G);
+    }
+  } else if (__builtin_expect(t0 < t1, 0)) {
     int run = 0;
-    for (int c = 0; c < a.b; c += 64) {
-      int raw = raw0, v = v0, incl = incl0;
-      if (c > 0) {
-        raw = (c + lane < a.b) ? a.lens[c + lane] : 0;
-        v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
-        incl = wave_incl_scan(v);
+    bool found = false;
+    for (int g0 = 0; g0 < nchunks && !found; g0 += kLensRegs) {
+      if (!lens_in_regs) load_chunks(g0);
+#pragma unroll
+      for (int k = 0; k < kLensRegs; ++k) {
+        if (g0 + k >= nchunks) break;
+        const int c = (g0 + k) * 64;
+        const int raw = rawr[k];
+        int v = v0, incl = incl0;
+        if (c > 0) {
+          v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
+          incl = wave_incl_scan(v);
+        }
+        int u, u_incl;
+        chunk_units(v, incl, u, u_incl);
+        const int lo = (run + u_incl - u) * a.G, hi = (run + u_incl) * a.G;
+        const uint64_t hit = __ballot(c + lane < a.b && u > 0 && lo <= t0 && t0 < hi);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          b_cur = c + src;
+          seg_base = __builtin_amdgcn_readfirstlane((run + __shfl(u_incl - u, src, 64)) * a.G);
+          cbase = c;
+          craw = raw;
+          found = true;
+          break;
+        }
+        run += __builtin_amdgcn_readlane(u_incl, 63);
       }
-      int u, u_incl;
-      chunk_units(v, incl, u, u_incl);
-      const int lo = (run + u_incl - u) * a.G, hi = (run + u_incl) * a.G;
-      const uint64_t hit = __ballot(c + lane < a.b && u > 0 && lo <= t0 && t0 < hi);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        b_cur = c + src;
-        seg_base = __builtin_amdgcn_readfirstlane((run + __shfl(u_incl - u, src, 64)) * a.G);
-        cbase = c;
-        craw = raw;
-        break;
-      }
-      run += __shfl(u_incl, 63, 64);
     }
     b_cur = __builtin_amdgcn_readfirstlane(b_cur);
   }

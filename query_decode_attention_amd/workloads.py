@@ -75,6 +75,16 @@ C4 = DecodeConfig("c4_gqa_b32_h64_g8_m32k", torch.bfloat16, b=32, h=64, G=8, dh=
 C5 = PrefillConfig("c5_prefill_b4_n4096", torch.bfloat16, b=4, n=4096, h=32, G=1, dh=128,
                    seed=1005)
 
+# The pages' own incremental-decoding speed setting (paper review, section 4.3
+# and Table 2): batch 1024, h = 8 heads of d_h = 128, every sequence at the
+# full length of 128 positions (the pages pad the self-attention K/V to the
+# maximum length, so every step costs the same); one appended row per step.
+# MQA, and the MHA comparison point (one K/V head per query head).
+PAPER_MQA = DecodeConfig("paper_mqa_b1024_h8_m128", torch.bfloat16, b=1024, h=8, G=1, dh=128,
+                         m_cap=128, lens_lo=127, lens_hi=127, append=True, seed=1021)
+PAPER_MHA = DecodeConfig("paper_mha_b1024_h8_m128", torch.bfloat16, b=1024, h=8, G=8, dh=128,
+                         m_cap=128, lens_lo=127, lens_hi=127, append=True, seed=1022)
+
 @dataclasses.dataclass(frozen=True)
 class BeamConfig:
     """Beam decoding: ``sources`` source sequences x ``beam`` hypotheses, each
