@@ -819,7 +819,10 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   constexpr int HPB = NT / kD4;          // heads per block
   constexpr int kBatch = 16;             // records per round trip
 
-  if (a.append && blockIdx.x == 0 && blockIdx.y == 0) {
+  // A block of its own (x = b*G, launched only when appending) bumps lens,
+  // so that no merge waits behind its load and store.
+  if ((int)blockIdx.x == a.b * a.G) {
+    if (blockIdx.y != 0) return;
     int over = 0;
     for (int bi = threadIdx.x; bi < a.b; bi += NT) {
       const int raw = a.lens[bi];
@@ -827,17 +830,23 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
       else over = 1;
     }
     if (over && a.err_flag) *a.err_flag = 1;
+    return;
   }
 
   const int seg = blockIdx.x;
   const int bi = seg / a.G, g = seg % a.G;
-  const int unit = a.prefix[bi + 1] - a.prefix[bi];  // lead-in units + tiles, or 0
+  // every header entry in one memory round trip, before any branch on them
+  // (readfirstlane keeps the loads ahead of the early return below)
+  const int p_bi = __builtin_amdgcn_readfirstlane(a.prefix[bi]);
+  const int p_next = __builtin_amdgcn_readfirstlane(a.prefix[bi + 1]);
+  const int p_total = __builtin_amdgcn_readfirstlane(a.prefix[a.b]);
+  const int lead = __builtin_amdgcn_readfirstlane(a.prefix[a.b + 2]);  // as the decode chose it
+  const int W = __builtin_amdgcn_readfirstlane(a.prefix[a.b + 3]);
+  const int unit = p_next - p_bi;      // lead-in units + tiles, or 0
   if (unit == 0) return;
-  const int lead = a.prefix[a.b + 2];      // as the decode chose it
-  const int W = a.prefix[a.b + 3];
   const int nb = unit - lead;
-  const int64_t Tt = (int64_t)a.prefix[a.b] * a.G;
-  const int64_t U0 = (int64_t)a.prefix[bi] * a.G + (int64_t)g * unit;  // first unit
+  const int64_t Tt = (int64_t)p_total * a.G;
+  const int64_t U0 = (int64_t)p_bi * a.G + (int64_t)g * unit;  // first unit
   const int64_t S0 = U0 + lead;                                           // first tile
   const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
@@ -985,7 +994,8 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   ca.rec_floats = a.rec_floats;
   ca.append = p.k_new != nullptr;
   constexpr int kHeadsPerBlock = kCombineThreads / (DH / 4);
-  dim3 cgrid((unsigned)(p.b * p.G), (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));
+  dim3 cgrid((unsigned)(p.b * p.G + (ca.append ? 1 : 0)),
+             (unsigned)((a.hg + kHeadsPerBlock - 1) / kHeadsPerBlock));
   hipLaunchKernelGGL((combine_kernel<T, DH, kCombineThreads>), cgrid, dim3(kCombineThreads), 0, s,
                      ca);
   return hipGetLastError();
