@@ -241,19 +241,41 @@ __device__ __forceinline__ void read_q(const u32x4 (*s_q)[64], int lane, u32x4 (
   for (int c = 0; c < NQ; ++c) qr[c] = s_q[c][lane];
 }
 
+// Where the Q^T chunks of a tile's score product come from: registers read
+// ahead (bf16), or LDS read chunk by chunk next to their product (fp32,
+// whose operands are too wide to hold all at once).
+struct QFromRegs {
+  const u32x4* r;
+  __device__ __forceinline__ u32x4 get(int c) const { return r[c]; }
+};
+struct QFromLds {
+  const u32x4 (*s)[64];
+  int lane;
+  __device__ __forceinline__ u32x4 get(int c) const { return s[c][lane]; }
+};
+
 // One decode tile: scores, online softmax with the tail masked at L, and P.V
 // with the V rows transposed in registers.
-template <typename T, int DH, bool FULL>
+template <typename T, int DH, bool FULL, typename QSrc>
 __device__ __forceinline__ void tile_update(WaveState<TileShape<T, DH>::ND>& st,
                                             const u32x4 (&kr)[TileShape<T, DH>::NQ],
                                             const u32x4 (&vr)[TileShape<T, DH>::NQ],
-                                            const u32x4 (&qr)[TileShape<T, DH>::NQ],
-                                            const SelOps<T>& sel, float scale_log2,
-                                            int pos0, int L, int half) {
+                                            const QSrc& q, const SelOps<T>& sel,
+                                            float scale_log2, int pos0, int L, int half) {
   constexpr int ND = TileShape<T, DH>::ND;
   constexpr int NQ = TileShape<T, DH>::NQ;
   constexpr int VTC = TileShape<T, DH>::VTC;
-  const f32x16 s = tile_scores<T, NQ>(kr, qr);
+  f32x16 s = {};
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const u32x4 qc = q.get(c);
+    if constexpr (sizeof(T) == 2) {
+      s = mfma_bf16(as_bf16x8(kr[c]), as_bf16x8(qc), s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma_f32(__uint_as_float(kr[c][e]), __uint_as_float(qc[e]), s);
+    }
+  }
   ProbTile<T> p;
   softmax_tile<T, ND, FULL>(st, s, scale_log2, pos0, L - 1, half, p);
   PvOps<T> pv;
@@ -634,9 +656,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const size_t base = seq_off + (size_t)pos0 * row_stride;
         load_kv<NQ, true>(a.k + base + lane_off, a.v + base + lane_off, true, 0, kr, vr);
         if (first_tile) __builtin_amdgcn_s_waitcnt(0x0F70);
-        read_q<NQ>(own_q, lane, qr);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_update<T, DH, true>(st, kr, vr, qr, sel, a.scale_log2, pos0, L, half);
+        if constexpr (sizeof(T) == 2) {
+          read_q<NQ>(own_q, lane, qr);
+          __builtin_amdgcn_sched_barrier(0);
+          tile_update<T, DH, true>(st, kr, vr, QFromRegs{qr}, sel, a.scale_log2, pos0, L, half);
+        } else {
+          tile_update<T, DH, true>(st, kr, vr, QFromLds{own_q, lane}, sel, a.scale_log2, pos0, L,
+                                   half);
+        }
       };
       bool q_landed = false;
       if (tile < te_whole) {
@@ -652,10 +679,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         q_landed = true;
         store_new_row(tile, kr, vr);
-        read_q<NQ>(own_q, lane, qr);
         // masked at L (a whole tile passes the mask unchanged)
-        tile_update<T, DH, false>(st, kr, vr, qr, sel, a.scale_log2, j0 + tile * kTileRows, L,
-                                  half);
+        if constexpr (sizeof(T) == 2) {
+          u32x4 qr[NQ];
+          read_q<NQ>(own_q, lane, qr);
+          tile_update<T, DH, false>(st, kr, vr, QFromRegs{qr}, sel, a.scale_log2,
+                                    j0 + tile * kTileRows, L, half);
+        } else {
+          tile_update<T, DH, false>(st, kr, vr, QFromLds{own_q, lane}, sel, a.scale_log2,
+                                    j0 + tile * kTileRows, L, half);
+        }
       }
       if (!q_landed) __builtin_amdgcn_s_waitcnt(0x0F70);  // no tile: the copy still lands
     }
