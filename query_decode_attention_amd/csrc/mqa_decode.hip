@@ -36,11 +36,11 @@
 // an agent-scope release per workgroup, i.e. a write-back of an XCD's whole
 // L2, which costs far more on gfx950 than a second small launch.
 //
-// Q.  Every wave copies its piece's Q^T operand with the direct-to-LDS load
-// into its own fold slot (free until the wave parks); the copy shares a
-// memory round trip with the wave's first tile, and no wave waits for
-// another.  From the second tile on, the Q^T reads from LDS are issued right
-// behind the tile's loads.
+// Q.  Every wave loads its piece's Q^T operand itself, so no wave waits for
+// another; the load shares a memory round trip with the wave's first tile.
+// bf16 keeps the operand in registers for the whole piece; fp32 (twice as
+// wide) copies it into the wave's own fold slot (free until the wave parks)
+// and reads it chunk by chunk.
 //
 // Fused append.  With k_new/v_new, sequence b attends over L_old + 1
 // positions; the row at L_old is read from k_new/v_new (never from the cache)
@@ -632,9 +632,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
       };
 
-      // Q^T of the piece into this wave's own fold slot; the copy shares its
-      // memory round trip with the first tile, whose wait covers it.
-      copy_q_own<T, DH>(a, own_q, bi, g, lane);
+      // Q^T of the piece: bf16 keeps it in registers for the whole piece (8
+      // loads, no LDS); fp32 (twice as wide) copies it into this wave's own
+      // fold slot.  Either way the loads share their memory round trip with
+      // the first tile, whose wait covers them.
+      u32x4 qreg[NQ];
+      if constexpr (sizeof(T) == 2) {
+        const char* qp = q_row(a, bi, g, lane, DH * sizeof(T));
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) qreg[c] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+      } else {
+        copy_q_own<T, DH>(a, own_q, bi, g, lane);
+      }
       // this lane's byte offset in a tile (row, 16-byte half), so that a
       // tile load is a uniform base plus one 32-bit offset per lane
       const uint32_t lane_off = (uint32_t)row * (uint32_t)row_stride + (uint32_t)half * 16u;
@@ -651,15 +660,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       // behind the tile's loads and complete while those are in flight.
       auto whole_tile = [&](bool first_tile) {
         const int pos0 = j0 + tile * kTileRows;
-        u32x4 kr[NQ], vr[NQ], qr[NQ];
+        u32x4 kr[NQ], vr[NQ];
         // uniform base of the tile plus a 32-bit offset per lane
         const size_t base = seq_off + (size_t)pos0 * row_stride;
         load_kv<NQ, true>(a.k + base + lane_off, a.v + base + lane_off, true, 0, kr, vr);
         if (first_tile) __builtin_amdgcn_s_waitcnt(0x0F70);
         if constexpr (sizeof(T) == 2) {
-          read_q<NQ>(own_q, lane, qr);
-          __builtin_amdgcn_sched_barrier(0);
-          tile_update<T, DH, true>(st, kr, vr, QFromRegs{qr}, sel, a.scale_log2, pos0, L, half);
+          tile_update<T, DH, true>(st, kr, vr, QFromRegs{qreg}, sel, a.scale_log2, pos0, L, half);
         } else {
           tile_update<T, DH, true>(st, kr, vr, QFromLds{own_q, lane}, sel, a.scale_log2, pos0, L,
                                    half);
@@ -681,9 +688,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         store_new_row(tile, kr, vr);
         // masked at L (a whole tile passes the mask unchanged)
         if constexpr (sizeof(T) == 2) {
-          u32x4 qr[NQ];
-          read_q<NQ>(own_q, lane, qr);
-          tile_update<T, DH, false>(st, kr, vr, QFromRegs{qr}, sel, a.scale_log2,
+          tile_update<T, DH, false>(st, kr, vr, QFromRegs{qreg}, sel, a.scale_log2,
                                     j0 + tile * kTileRows, L, half);
         } else {
           tile_update<T, DH, false>(st, kr, vr, QFromLds{own_q, lane}, sel, a.scale_log2,
