@@ -402,6 +402,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // which fix the lead-in.  raw0 / v0 / incl0: lens entry, tiles and their
   // inclusive prefix for sequence `lane` (the first 64), reused below.
   int tiles = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
+  // per chunk (lane = chunk index, up to 64 chunks): tiles and non-empty
+  // sequences before it, so that the range search needs one chunk only
+  int ch_t = 0, ch_ne = 0;
   if (nchunks == 1) {  // b <= 64: one chunk, a compact path
     raw0 = lane < a.b ? a.lens[lane] : 0;
     v0 = lane < a.b ? tiles_of(seq_view_raw(a, raw0)) : 0;
@@ -422,6 +425,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         raw0 = rawr[k];
         v0 = v;
         incl0 = incl;
+      }
+      if (lane == g0 + k) {
+        ch_t = tiles;
+        ch_ne = nonempty;
       }
       tiles += __builtin_amdgcn_readlane(incl, 63);
       nonempty += __popcll(__ballot(v > 0));
@@ -462,6 +469,34 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const int src = __builtin_ctzll(hit);
       b_cur = __builtin_amdgcn_readfirstlane(src);
       seg_base = __builtin_amdgcn_readfirstlane(__shfl(u_incl - u, src, 64) * a.G);
+    }
+  } else if (__builtin_expect(t0 < t1 && nchunks <= 64, 0)) {
+    // the chunk holding unit t0 from the per-chunk prefixes, then one scan
+    const int u_before = ch_t + lead * ch_ne;  // units (per group) before chunk `lane`
+    const uint64_t cm = __ballot(lane < nchunks && u_before * a.G <= t0);
+    const int kh = 63 - __builtin_clzll(cm);
+    const int c = kh * 64;
+    const int run = __builtin_amdgcn_readlane(u_before, kh);
+    int raw = 0;
+    if (lens_in_regs) {
+#pragma unroll
+      for (int k = 0; k < kLensRegs; ++k)
+        if (k == kh) raw = rawr[k];
+    } else {
+      raw = a.lens[c + lane < a.b ? c + lane : a.b - 1];
+    }
+    const int v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
+    const int incl = wave_incl_scan(v);
+    int u, u_incl;
+    chunk_units(v, incl, u, u_incl);
+    const int lo = (run + u_incl - u) * a.G, hi = (run + u_incl) * a.G;
+    const uint64_t hit = __ballot(c + lane < a.b && u > 0 && lo <= t0 && t0 < hi);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      b_cur = __builtin_amdgcn_readfirstlane(c + src);
+      seg_base = __builtin_amdgcn_readfirstlane((run + __shfl(u_incl - u, src, 64)) * a.G);
+      cbase = c;
+      craw = raw;
     }
   } else if (__builtin_expect(t0 < t1, 0)) {
     int run = 0;
