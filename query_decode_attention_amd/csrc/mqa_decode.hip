@@ -542,7 +542,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       cbase = bi;
       craw = (bi + lane < a.b) ? a.lens[bi + lane] : 0;
     }
-    return __shfl(craw, bi - cbase, 64);
+    return __builtin_amdgcn_readlane(craw, bi - cbase);  // uniform lane: no LDS trip
   };
 
   // A piece is the part of one (sequence, group) segment inside this
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         continue;
       }
       const int unit = nb + lead;  // units of one group of this sequence
-      const int g = (t - seg_base) / unit;
+      const int g = a.G == 1 ? 0 : (t - seg_base) / unit;  // MQA: no division
       const int seg0 = seg_base + g * unit + lead;  // its first tile
       const int ta = (t > seg0 ? t : seg0) - seg0;
       const int te = (t1 < seg0 + nb ? t1 : seg0 + nb) - seg0;
