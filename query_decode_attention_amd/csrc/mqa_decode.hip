@@ -154,16 +154,20 @@ static_assert(kSegLead <= kMaxSegLead, "lead-in within the unit-index bound");
 constexpr int kSmallUnits = 4;
 
 // Workgroups that share the Tv units of `segs` non-empty segments: the
-// launched grid, but no more than one per `min_units` units unless there are
-// more segments than that (short segments are better run side by side than
-// one after another), and no more than Tv / (lead + 1), so that every range
-// of units holds at least one tile.  The combine reads the value back.
-__device__ __forceinline__ int effective_grid(int64_t Tv, int64_t segs, int grid, int min_units,
-                                             int lead) {
-  int64_t w = (Tv + min_units - 1) / min_units;
-  if (w < segs) w = segs;
-  if (w > grid) w = grid;
-  if (w > Tv / (lead + 1)) w = Tv / (lead + 1);
+// launched grid, but no more than one per kSmallUnits units of a small step
+// (one per NW units otherwise) unless there are more segments than that
+// (short segments are better run side by side than one after another), and
+// no more than Tv / (lead + 1), so that every range of units holds at least
+// one tile.  The combine reads the value back.  32-bit arithmetic with
+// constant divisors (Tv < 2^30 by the shape check).
+template <int NW>
+__device__ __forceinline__ int effective_grid(int Tv, int segs, int grid, bool small_step) {
+  const unsigned T = (unsigned)Tv;
+  unsigned w = small_step ? (T + kSmallUnits - 1) / kSmallUnits : (T + NW - 1) / NW;
+  if (w < (unsigned)segs) w = (unsigned)segs;
+  if (w > (unsigned)grid) w = (unsigned)grid;
+  const unsigned cap = small_step ? T : T / (kSegLead + 1);  // small steps have no lead-in
+  if (w > cap) w = cap;
   return (int)(w < 1 ? 1 : w);
 }
 
@@ -173,11 +177,19 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// First unit of workgroup w out of W over T units.
-__device__ __forceinline__ int64_t wg_start(int64_t T, int w, int W) { return T * w / W; }
-// Workgroup whose range contains unit t (T > 0).
-__device__ __forceinline__ int wg_of(int64_t t, int64_t T, int W) {
-  return (int)(((t + 1) * W + T - 1) / T) - 1;
+// First unit of workgroup w out of W over T units, floor(T * w / W), and the
+// workgroup whose range holds unit t (T > 0), ceil((t + 1) * W / T) - 1.
+// With T < 2^30 and W <= kMaxDecodeGrid (2^11) both products are exact in a
+// double, and a correctly rounded quotient cannot cross an integer (a
+// non-integer quotient lies at least 1/W resp. 1/T from one, far more than
+// its rounding error), so floor / ceil of the double quotient are exact; the
+// double divide is much shorter than a 64-bit integer one.
+static_assert(kMaxDecodeGrid <= 2048, "exact double quotients below need W <= 2^11");
+__device__ __forceinline__ int wg_start(int T, int w, int W) {
+  return (int)((double)T * (double)w / (double)W);
+}
+__device__ __forceinline__ int wg_of(int t, int T, int W) {
+  return (int)__builtin_ceil((double)(t + 1) * (double)W / (double)T) - 1;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
@@ -446,8 +458,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int segs = nonempty * a.G;
   // Workgroups in use (see effective_grid): every wave has work, short
   // segments still run side by side.
-  const int W = effective_grid(Tt, segs, gridDim.x, small ? kSmallUnits : NW, lead);
-  const int t0 = (int)wg_start(Tt, blockIdx.x, W), t1 = (int)wg_start(Tt, blockIdx.x + 1, W);
+  const int W = effective_grid<NW>(Tt, segs, gridDim.x, small);
+  const int t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
   // Units of the sequences of one chunk: their tiles plus `lead` per non-empty
   // sequence; u_excl / u_incl are prefixes within the chunk.
   auto chunk_units = [&](int v, int incl, int& u, int& u_incl) {
@@ -918,9 +930,9 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   const int unit = p_next - p_bi;      // lead-in units + tiles, or 0
   if (unit == 0) return;
   const int nb = unit - lead;
-  const int64_t Tt = (int64_t)p_total * a.G;
-  const int64_t U0 = (int64_t)p_bi * a.G + (int64_t)g * unit;  // first unit
-  const int64_t S0 = U0 + lead;                                           // first tile
+  const int Tt = p_total * a.G;  // units (below 2^30 by the shape check)
+  const int U0 = p_bi * a.G + g * unit;  // first unit
+  const int S0 = U0 + lead;              // first tile
   const int wf = wg_of(S0, Tt, W), wl = wg_of(S0 + nb - 1, Tt, W);
   if (wf == wl) return;  // one workgroup covered the segment and wrote it
   // wf's range began in an earlier segment (whose last tile is unit U0 - 1)
