@@ -387,14 +387,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   u32x4 (*const own_q)[64] = reinterpret_cast<u32x4 (*)[64]>(&s_slot[wave]);
 
   // ---- schedule (each wave on its own) ----
-  // lens is read kLensRegs chunks of 64 entries at a time with all loads in
-  // flight together (one memory round trip per 1024 sequences, not one per
-  // 64); when b <= 64 * kLensRegs the entries stay in registers for the
-  // search below.
+  // Three layouts of lens in the wave, by batch size: b <= 64, one entry per
+  // lane; 64 < b <= 64 * kLensRegs ("block"), lane l holds the kLensRegs
+  // consecutive entries from kLensRegs * l, so one round trip and one scan
+  // over the lanes' block sums give every prefix; larger b, chunks of 64
+  // entries (one per lane), read kLensRegs chunks at a time with all loads in
+  // flight together (one memory round trip per 1024 sequences).
   constexpr int kLensRegs = 16;
+  static_assert(kLensRegs == 16, "the block layout indexes lanes with >> 4");
   const int nchunks = (a.b + 63) / 64;
-  const bool lens_in_regs = nchunks <= kLensRegs;
+  const bool blk = nchunks > 1 && nchunks <= kLensRegs;
   int rawr[kLensRegs];
+  auto load_block = [&]() {
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      const int i = kLensRegs * lane + k;
+      rawr[k] = a.lens[i < a.b ? i : a.b - 1];  // clamped: no branch between the loads
+    }
+  };
+  // units of entry k of this lane's block in the block layout (0 past b)
+  auto blk_tiles = [&](int k) {
+    return kLensRegs * lane + k < a.b ? tiles_of(seq_view_raw(a, rawr[k])) : 0;
+  };
   auto load_chunks = [&](int g0) {
     // unconditional loads of clamped indices (no branch between them, so they
     // are all in flight together); entries past b read as 0
@@ -411,11 +425,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       if ((g0 + k) * 64 + lane >= a.b) rawr[k] = 0;
   };
   // Pass 1: tiles of every sequence (per group) and the non-empty count,
-  // which fix the lead-in.  raw0 / v0 / incl0: lens entry, tiles and their
-  // inclusive prefix for sequence `lane` (the first 64), reused below.
+  // which fix the lead-in.  raw0 / v0 / incl0 (not in the block layout): lens
+  // entry, tiles and their inclusive prefix for sequence `lane` (the first
+  // 64), reused below.
   int tiles = 0, nonempty = 0, raw0 = 0, v0 = 0, incl0 = 0;
-  // per chunk (lane = chunk index, up to 64 chunks): tiles and non-empty
-  // sequences before it, so that the range search needs one chunk only
+  // Tiles and non-empty sequences before lane's block (block layout) or
+  // before chunk `lane` (chunk layout, up to 64 chunks), so that the range
+  // search needs one block or chunk only.
   int ch_t = 0, ch_ne = 0;
   if (nchunks == 1) {  // b <= 64: one chunk, a compact path
     raw0 = lane < a.b ? a.lens[lane] : 0;
@@ -424,7 +440,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     tiles = __builtin_amdgcn_readlane(incl0, 63);
     nonempty = __popcll(__ballot(v0 > 0));
   }
-  if (__builtin_expect(nchunks > 1, 0)) {
+  if (__builtin_expect(blk, 0)) {
+    load_block();
+    int bt = 0, bne = 0;
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      const int v = blk_tiles(k);
+      bt += v;
+      bne += v > 0 ? 1 : 0;
+    }
+    const int it = wave_incl_scan(bt), ine = wave_incl_scan(bne);
+    ch_t = it - bt;
+    ch_ne = ine - bne;
+    tiles = __builtin_amdgcn_readlane(it, 63);
+    nonempty = __builtin_amdgcn_readlane(ine, 63);
+  }
+  if (__builtin_expect(nchunks > kLensRegs, 0)) {
   for (int g0 = 0; g0 < nchunks; g0 += kLensRegs) {
     load_chunks(g0);
 #pragma unroll
@@ -482,6 +513,39 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       b_cur = __builtin_amdgcn_readfirstlane(src);
       seg_base = __builtin_amdgcn_readfirstlane(__shfl(u_incl - u, src, 64) * a.G);
     }
+  } else if (__builtin_expect(t0 < t1 && blk, 0)) {
+    // the block holding unit t0 from the per-block prefixes, then a uniform
+    // walk over its entries (read from lane kh)
+    const int u_before = ch_t + lead * ch_ne;  // units (per group) before lane's block
+    const uint64_t cm = __ballot(kLensRegs * lane < a.b && u_before * a.G <= t0);
+    const int kh = 63 - __builtin_clzll(cm);
+    int run = __builtin_amdgcn_readlane(u_before, kh);
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      const int bi = kLensRegs * kh + k;
+      const int raw = __builtin_amdgcn_readlane(rawr[k], kh);
+      const int v = bi < a.b ? tiles_of(seq_view_raw(a, raw)) : 0;
+      const int u = v > 0 ? v + lead : 0;
+      if (u > 0 && t0 < (run + u) * a.G) {
+        b_cur = bi;
+        seg_base = run * a.G;
+        break;
+      }
+      run += u;
+    }
+    b_cur = __builtin_amdgcn_readfirstlane(b_cur);
+    seg_base = __builtin_amdgcn_readfirstlane(seg_base);
+    // the lane cache below (entries b_cur .. b_cur + 63) from the blocks:
+    // entry j sits in register j % 16 of lane j / 16
+    const int j = b_cur + lane;
+    int x = 0;
+#pragma unroll
+    for (int k = 0; k < kLensRegs; ++k) {
+      const int y = __builtin_amdgcn_ds_bpermute(((j >> 4) & 63) << 2, rawr[k]);
+      if ((j & (kLensRegs - 1)) == k) x = y;
+    }
+    cbase = b_cur;
+    craw = j < a.b ? x : 0;
   } else if (__builtin_expect(t0 < t1 && nchunks <= 64, 0)) {
     // the chunk holding unit t0 from the per-chunk prefixes, then one scan
     const int u_before = ch_t + lead * ch_ne;  // units (per group) before chunk `lane`
@@ -489,14 +553,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int kh = 63 - __builtin_clzll(cm);
     const int c = kh * 64;
     const int run = __builtin_amdgcn_readlane(u_before, kh);
-    int raw = 0;
-    if (lens_in_regs) {
-#pragma unroll
-      for (int k = 0; k < kLensRegs; ++k)
-        if (k == kh) raw = rawr[k];
-    } else {
-      raw = a.lens[c + lane < a.b ? c + lane : a.b - 1];
-    }
+    const int raw = a.lens[c + lane < a.b ? c + lane : a.b - 1];
     const int v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, raw)) : 0;
     const int incl = wave_incl_scan(v);
     int u, u_incl;
@@ -514,7 +571,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     int run = 0;
     bool found = false;
     for (int g0 = 0; g0 < nchunks && !found; g0 += kLensRegs) {
-      if (!lens_in_regs) load_chunks(g0);
+      load_chunks(g0);
 #pragma unroll
       for (int k = 0; k < kLensRegs; ++k) {
         if (g0 + k >= nchunks) break;
@@ -838,17 +895,41 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // of sequences with nothing visible.  Both are stores; they come after the
   // streaming, because a wave's loads wait for the stores it issued earlier.
   if (blockIdx.x == 0 && wave == 0) {  // the units prefix, for the combine
-    int run = 0;
-    for (int c = 0; c < a.b; c += 64) {
-      int v = v0, incl = incl0;
-      if (c > 0) {
-        v = (c + lane < a.b) ? tiles_of(seq_view(a, c + lane)) : 0;
-        incl = wave_incl_scan(v);
+    if (blk) {  // one round trip and one scan, as in pass 1
+      load_block();
+      int uk[kLensRegs], s = 0;
+#pragma unroll
+      for (int k = 0; k < kLensRegs; ++k) {
+        const int v = blk_tiles(k);
+        uk[k] = v > 0 ? v + lead : 0;
+        s += uk[k];
       }
-      int u, u_incl;
-      chunk_units(v, incl, u, u_incl);
-      if (c + lane < a.b) a.prefix[c + lane] = run + u_incl - u;
-      run += __shfl(u_incl, 63, 64);
+      int run = wave_incl_scan(s) - s;
+#pragma unroll
+      for (int k = 0; k < kLensRegs; ++k) {
+        const int i = kLensRegs * lane + k;
+        if (i < a.b) a.prefix[i] = run;
+        run += uk[k];
+      }
+    } else {  // one chunk per lane set; up to kLensRegs chunks per round trip
+      int run = 0;
+      for (int g0 = 0; g0 < nchunks; g0 += kLensRegs) {
+        if (nchunks > 1) load_chunks(g0);
+#pragma unroll
+        for (int k = 0; k < kLensRegs; ++k) {
+          if (g0 + k >= nchunks) break;
+          const int c = (g0 + k) * 64;
+          int v = v0, incl = incl0;
+          if (nchunks > 1) {
+            v = (c + lane < a.b) ? tiles_of(seq_view_raw(a, rawr[k])) : 0;
+            incl = wave_incl_scan(v);
+          }
+          int u, u_incl;
+          chunk_units(v, incl, u, u_incl);
+          if (c + lane < a.b) a.prefix[c + lane] = run + u_incl - u;
+          run += __builtin_amdgcn_readlane(u_incl, 63);
+        }
+      }
     }
     if (lane == 0) {
       a.prefix[a.b] = total;
@@ -861,14 +942,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // Sequences with nothing visible get zeros; wave k of workgroup 0 checks
   // sequences k*64 .. k*64+63, NW*64 at a time, and writes their rows.
   if (blockIdx.x == 0) {
-    for (int c = wave * 64; c < a.b; c += NW * 64) {
-      const int raw = c == 0 ? raw0 : (c + lane < a.b ? a.lens[c + lane] : 0);
-      uint64_t empty = __ballot(c + lane < a.b && tiles_of(seq_view_raw(a, raw)) == 0);
-      while (empty) {
-        const int bi = c + __builtin_ctzll(empty);
-        empty &= empty - 1;
-        T* op = reinterpret_cast<T*>(a.o) + (size_t)bi * a.h * DH;
-        for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
+    constexpr int kZ = 4;  // chunks per round trip
+    for (int c0 = wave * 64; c0 < a.b; c0 += kZ * NW * 64) {
+      int rz[kZ];
+#pragma unroll
+      for (int z = 0; z < kZ; ++z) {
+        const int c = c0 + z * NW * 64, i = c + lane;
+        rz[z] = 0;
+        if (c == 0 && nchunks == 1) rz[z] = raw0;
+        else if (c < a.b) rz[z] = a.lens[i < a.b ? i : a.b - 1];
+      }
+#pragma unroll
+      for (int z = 0; z < kZ; ++z) {
+        const int c = c0 + z * NW * 64;
+        if (c >= a.b) break;
+        uint64_t empty = __ballot(c + lane < a.b && tiles_of(seq_view_raw(a, rz[z])) == 0);
+        while (empty) {
+          const int bi = c + __builtin_ctzll(empty);
+          empty &= empty - 1;
+          T* op = reinterpret_cast<T*>(a.o) + (size_t)bi * a.h * DH;
+          for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
   }
