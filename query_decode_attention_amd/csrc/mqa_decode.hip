@@ -129,10 +129,6 @@ __device__ __forceinline__ SeqView seq_view_raw(const DecodeArgs& a, int raw) {
   return s;
 }
 
-__device__ __forceinline__ SeqView seq_view(const DecodeArgs& a, int bi) {
-  return seq_view_raw(a, a.lens[bi]);
-}
-
 __device__ __forceinline__ int tiles_of(const SeqView& s) {
   return (s.L - s.j0 + kTileRows - 1) / kTileRows;
 }
