@@ -125,6 +125,22 @@ def test_decode_short_sequences_several_rounds_gqa_d128():
     assert_parity(o, ref, torch.float32, "b=1500 G=2 fp32 short")
 
 
+@pytest.mark.parametrize("b", [65, 1024, 1025])
+@pytest.mark.parametrize("append", [False, True])
+def test_decode_lens_layout_boundaries(b, append):
+    """Batch sizes at the edges of the schedule's lens layouts (one entry per
+    lane up to 64, lane blocks of 16 up to 1024, chunks of 64 beyond), with
+    empty rows mixed in and two groups."""
+    announce(f"decode layout boundary b={b} append={append}")
+    cfg, inp = make(torch.bfloat16, b, 8, 2, 64, 100, 0, 99, seed=7400 + b + append)
+    lens = inp["lens"].clone()
+    lens[::7] = 0  # rows with nothing visible (one visible row after an append)
+    inp["lens"] = lens
+    o, _ = run_decode(inp, cfg.scale, append=append)
+    ref, _ = oracle_step(inp, cfg.scale, append=append)
+    assert_parity(o, ref, torch.bfloat16, f"layout boundary b={b}")
+
+
 @pytest.mark.parametrize("window", [1, 7, 32, 33, 5000])
 def test_decode_local_window(window):
     """Local attention over the last `window` positions (current + 31 previous is 32)."""
