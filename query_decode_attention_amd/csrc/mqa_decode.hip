@@ -381,6 +381,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
   const int row = lane & 31, half = lane >> 5;
   u32x4 (*const own_q)[64] = reinterpret_cast<u32x4 (*)[64]>(&s_slot[wave]);
+  // lane constants of the V transpose (for b <= 64 set up while lens is in
+  // flight, otherwise after the schedule)
+  SelOps<T> sel;
 
   // ---- schedule (each wave on its own) ----
   // Three layouts of lens in the wave, by batch size: b <= 64, one entry per
@@ -431,6 +434,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   int ch_t = 0, ch_ne = 0;
   if (nchunks == 1) {  // b <= 64: one chunk, a compact path
     raw0 = lane < a.b ? a.lens[lane] : 0;
+    sel.init(row, half);
+    sel.pin();
     v0 = lane < a.b ? tiles_of(seq_view_raw(a, raw0)) : 0;
     incl0 = wave_incl_scan(v0);
     tiles = __builtin_amdgcn_readlane(incl0, 63);
@@ -598,8 +603,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 
 
-  SelOps<T> sel;
-  sel.init(row, half);
+  if (nchunks != 1) sel.init(row, half);
   const size_t row_stride = (size_t)a.G * DH * sizeof(T);
   // lens entry of sequence bi (uniform), refilling the lane cache by chunks
   auto raw_of = [&](int bi) {

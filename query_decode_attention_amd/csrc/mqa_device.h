@@ -149,6 +149,9 @@ template <> struct SelOps<__bf16> {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[a][e] = (__bf16)((n == 16 * a + 8 * half + e) ? 1.0f : 0.0f);
   }
+  // Keeps the set-up where it is written, after the memory requests before
+  // it (the compiler would otherwise sink it to the first use).
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(s[0]), "+v"(s[1]) : : "memory"); }
 };
 template <> struct SelOps<float> {
   float s[4][4];
@@ -157,6 +160,12 @@ template <> struct SelOps<float> {
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[a][e] = (n == 8 * a + 4 * half + e) ? 1.0f : 0.0f;
+  }
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(s[a][e]) : : "memory");
   }
 };
 
