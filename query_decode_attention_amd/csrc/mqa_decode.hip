@@ -688,14 +688,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       p_ws = wave_incl_scan(p_w) - p_w;
     }
     // this wave's piece, or -1 (more waves than tiles)
-    const int pw = wave < used ? __popcll(__ballot(lane < np && p_ws <= wave)) - 1 : -1;
+    const int pw = wave >= used ? -1 : np == 1 ? 0 : __popcll(__ballot(lane < np && p_ws <= wave)) - 1;
     // For the fold: bit w of `runs` is set where a run of waves (a piece, or
     // the waves without one) starts; lane p of p_flags says whether piece p
     // is a whole segment (bit 0) and which record slot it takes (bit 1).
-    int runs = used < NW ? 1 << used : 0;
+    int runs = (used < NW ? 1 << used : 0) | 1;  // piece 0 starts at wave 0
+    if (np > 1) {
 #pragma unroll
-    for (int x = 0; x < NW; ++x)
-      if (__ballot(lane < np && p_ws == x)) runs |= 1 << x;
+      for (int x = 1; x < NW; ++x)
+        if (__ballot(lane < np && p_ws == x)) runs |= 1 << x;
+    }
     const int p_flags =
         ((p_ta == 0 && p_te == p_nb) ? 1 : 0) | ((first_round && lane == 0) ? 0 : 2);
 
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         for (tile += step; tile < te_whole; tile += step) whole_tile(false);
       }
       if (special && tile == te - 1) {
-        u32x4 kr[NQ], vr[NQ], qr[NQ];
+        u32x4 kr[NQ], vr[NQ];
         const char *kp, *vp;
         const bool valid = row_ptrs(tile, kp, vp);
         load_kv<NQ, false>(kp, vp, valid, half, kr, vr);
@@ -1013,14 +1015,19 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   }
 
   const int seg = blockIdx.x;
-  const int bi = seg / a.G, g = seg % a.G;
-  // every header entry in one memory round trip, before any branch on them
-  // (readfirstlane keeps the loads ahead of the early return below)
-  const int p_bi = __builtin_amdgcn_readfirstlane(a.prefix[bi]);
-  const int p_next = __builtin_amdgcn_readfirstlane(a.prefix[bi + 1]);
-  const int p_total = __builtin_amdgcn_readfirstlane(a.prefix[a.b]);
-  const int lead = __builtin_amdgcn_readfirstlane(a.prefix[a.b + 2]);  // as the decode chose it
-  const int W = __builtin_amdgcn_readfirstlane(a.prefix[a.b + 3]);
+  const int bi = a.G == 1 ? seg : seg / a.G, g = a.G == 1 ? 0 : seg % a.G;
+  // every header entry in one memory round trip, before any branch on them:
+  // scalar loads (the header is uniform and read-only here)
+  using cint = const __attribute__((address_space(4))) int32_t;
+  cint* const hdr = (cint*)(a.prefix);
+  const int p_bi = hdr[bi];
+  const int p_next = hdr[bi + 1];
+  const int p_total = hdr[a.b];
+  const int lead = hdr[a.b + 2];  // as the decode chose it
+  const int W = hdr[a.b + 3];
+  // (kept ahead of the early return: the compiler would sink the loads of
+  // the last three below it, a second round trip)
+  asm volatile("" : : "s"(p_bi), "s"(p_next), "s"(p_total), "s"(lead), "s"(W));
   const int unit = p_next - p_bi;      // lead-in units + tiles, or 0
   if (unit == 0) return;
   const int nb = unit - lead;
