@@ -75,15 +75,53 @@ C4 = DecodeConfig("c4_gqa_b32_h64_g8_m32k", torch.bfloat16, b=32, h=64, G=8, dh=
 C5 = PrefillConfig("c5_prefill_b4_n4096", torch.bfloat16, b=4, n=4096, h=32, G=1, dh=128,
                    seed=1005)
 
-# The pages' own incremental-decoding speed setting (paper review, section 4.3
-# and Table 2): batch 1024, h = 8 heads of d_h = 128, every sequence at the
-# full length of 128 positions (the pages pad the self-attention K/V to the
-# maximum length, so every step costs the same); one appended row per step.
-# MQA, and the MHA comparison point (one K/V head per query head).
+# The pages' own incremental-decoding speed setting (study notes, section
+# 6.2, which reports the paper's section 4.3 and Table 2): batch 1024, h = 8
+# heads of d_h = 128, length 128, with the decoder self-attention K/V padded
+# to the full length of 128 so that every step costs the same.  One step here
+# is the attention over all 128 positions (decode only, no append).  MQA, and
+# the MHA comparison point (one K/V head per query head).
 PAPER_MQA = DecodeConfig("paper_mqa_b1024_h8_m128", torch.bfloat16, b=1024, h=8, G=1, dh=128,
-                         m_cap=128, lens_lo=127, lens_hi=127, append=True, seed=1021)
+                         m_cap=128, lens_lo=128, lens_hi=128, append=False, seed=1021)
 PAPER_MHA = DecodeConfig("paper_mha_b1024_h8_m128", torch.bfloat16, b=1024, h=8, G=8, dh=128,
-                         m_cap=128, lens_lo=127, lens_hi=127, append=True, seed=1022)
+                         m_cap=128, lens_lo=128, lens_hi=128, append=False, seed=1022)
+
+
+@dataclasses.dataclass(frozen=True)
+class SerialConfig:
+    """Serial incremental decoding of ``tokens`` output tokens for ``b``
+    sequences through ``layers`` decoder self-attention layers: every token
+    appends one K/V row per sequence and layer and attends over the cache
+    grown so far (1, 2, ..., tokens positions), so the whole loop re-reads
+    sum_{t<=n} t = n(n+1)/2 cached positions (study notes, section 1.2).
+    ``window`` > 0 is local attention over the last ``window`` positions."""
+    name: str
+    dtype: torch.dtype
+    b: int
+    h: int
+    G: int
+    dh: int
+    tokens: int
+    layers: int
+    window: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dh)
+
+
+# The pages' decoder at its speed setting (study notes, sections 6.1 and 6.2:
+# 6 decoder layers, batch 1024, h = 8, d_k = d_v = 128, target length 128;
+# the local variant attends over the current position and the 31 before it).
+SERIAL_MQA = SerialConfig("serial_mqa_b1024_h8_n128_l6", torch.bfloat16, b=1024, h=8, G=1,
+                          dh=128, tokens=128, layers=6, window=0, seed=1031)
+SERIAL_MHA = SerialConfig("serial_mha_b1024_h8_n128_l6", torch.bfloat16, b=1024, h=8, G=8,
+                          dh=128, tokens=128, layers=6, window=0, seed=1032)
+SERIAL_LOCAL_MQA = SerialConfig("serial_local_mqa_b1024_h8_n128_l6_w32", torch.bfloat16, b=1024,
+                                h=8, G=1, dh=128, tokens=128, layers=6, window=32, seed=1033)
+SERIAL_LOCAL_MHA = SerialConfig("serial_local_mha_b1024_h8_n128_l6_w32", torch.bfloat16, b=1024,
+                                h=8, G=8, dh=128, tokens=128, layers=6, window=32, seed=1034)
 
 @dataclasses.dataclass(frozen=True)
 class BeamConfig:

@@ -106,3 +106,55 @@ def test_attend_argument_errors_raise():
     K96 = torch.zeros(1, 3, 1, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(mqa.MQAError):
         mqa.attend(Q96, K96, K96, 1.0)             # d_h = 96: rejected by the library
+
+
+# Unmasked attention takes the folded softmax for a positive scale and the
+# unfolded one for zero or a negative scale; masked attention never folds.
+# Each instance is run with a scale <= 0 and with very large logits.
+SCALE_GRID = [
+    # dtype, b, n, m, h, G, dh, mask, scale
+    (torch.bfloat16, 2, 9, 70, 32, 1, 128, "none", 0.0),
+    (torch.bfloat16, 1, 30, 45, 8, 2, 64, "none", -0.25),
+    (torch.float32, 2, 7, 100, 16, 1, 128, "none", 0.0),
+    (torch.float32, 1, 12, 33, 32, 4, 64, "none", -0.1),
+    (torch.bfloat16, 2, 6, 90, 32, 1, 128, "pad", 0.0),
+    (torch.bfloat16, 1, 5, 64, 8, 8, 128, "full_inf", -0.2),
+]
+
+
+@pytest.mark.parametrize("dtype,b,n,m,h,G,dh,kind,scale", SCALE_GRID)
+def test_attend_nonpositive_scale(dtype, b, n, m, h, G, dh, kind, scale):
+    what = f"attend scale {scale} {dtype} b={b} n={n} m={m} h={h} G={G} dh={dh} mask={kind}"
+    announce(what)
+    cfg = W.MemoryConfig("t", dtype, b, n, m, h, G, dh, m, m, 420 + n + m)
+    inp = W.memory_inputs(cfg)
+    mask = make_mask(kind, b, h, n, m, 421 + m)
+    out = mqa.attend(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), scale,
+                     mask=None if mask is None else mask.cuda())
+    torch.cuda.synchronize()
+    ref = oracle_ref(inp["Q"], inp["K"], inp["V"], scale, mask)
+    assert_parity(out, ref, dtype, what)
+    if scale == 0.0 and kind == "none":
+        # equal weights: every query row is the mean of the group's V rows
+        mean = inp["V"].double().mean(dim=1, keepdim=True).repeat_interleave(h // G, dim=2)
+        assert_parity(out, mean.expand(b, n, h, dh).numpy(), dtype, what + " = mean of V")
+
+
+@pytest.mark.parametrize("kind", ["none", "pad", "full"])
+@pytest.mark.parametrize("scale_sign", [1.0, -1.0])
+def test_attend_large_logits(kind, scale_sign):
+    """Q x 20 on every attend instance: folded (positive scale, no mask),
+    unfolded (negative scale), per-key mask and general mask."""
+    b, n, m, h, G, dh = 2, 21, 150, 32, 1, 128
+    what = f"attend Q x 20 mask={kind} scale sign {scale_sign}"
+    announce(what)
+    cfg = W.MemoryConfig("t", torch.bfloat16, b, n, m, h, G, dh, m, m, 430 + len(kind))
+    inp = W.memory_inputs(cfg)
+    inp["Q"] = (inp["Q"].float() * 20).to(torch.bfloat16)
+    mask = make_mask(kind, b, h, n, m, 431)
+    scale = scale_sign * cfg.scale
+    out = mqa.attend(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), scale,
+                     mask=None if mask is None else mask.cuda())
+    torch.cuda.synchronize()
+    ref = oracle_ref(inp["Q"], inp["K"], inp["V"], scale, mask)
+    assert_parity(out, ref, torch.bfloat16, what)

@@ -87,3 +87,50 @@ def test_prefill_fills_cache_and_hands_off_to_decode():
         ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], cfg.scale, rows=[t, 150 + t])
         assert_parity(o, ref, torch.bfloat16, f"decode row {t}")
         assert_parity(O[:, t], ref, torch.bfloat16, f"prefill row {t}")
+
+
+# Instances chosen by the scale's sign: a positive scale folds the scale into
+# the exponent (max over raw scores); zero or a negative scale takes the
+# unfolded softmax.  Both must match the oracle on the same inputs.
+SCALE_CASES = [
+    # dtype, b, n, h, G, dh, scale
+    (torch.bfloat16, 2, 75, 32, 1, 128, 0.0),
+    (torch.bfloat16, 2, 75, 32, 1, 128, -0.3),
+    (torch.bfloat16, 1, 130, 16, 2, 64, 0.0),     # h/G = 8: four rows per wave
+    (torch.bfloat16, 1, 66, 4, 4, 128, -0.09),    # MHA: 32 rows per wave
+    (torch.float32, 1, 70, 8, 1, 64, 0.0),
+    (torch.float32, 2, 41, 32, 1, 128, -0.2),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES,
+                         ids=lambda c: f"{str(c[0])[6:]}-n{c[2]}h{c[3]}G{c[4]}d{c[5]}-s{c[6]}")
+def test_prefill_nonpositive_scale(case):
+    dtype, b, n, h, G, dh, scale = case
+    announce(f"prefill scale {scale} {case}")
+    cfg, inp = make(dtype, b, n, h, G, dh, seed=8300 + n + h)
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], scale)
+    assert_parity(O, ref, dtype, f"prefill scale {scale} {case}")
+    if scale == 0.0:
+        # every weight is equal: row t is the mean of V rows 0..t of its group
+        Vd = inp["V"].double()
+        csum = Vd.cumsum(dim=1) / torch.arange(1, n + 1, dtype=torch.float64).view(1, n, 1, 1)
+        mean = csum.repeat_interleave(h // G, dim=2)
+        assert_parity(O, mean.numpy(), dtype, "prefill scale 0 = running mean of V")
+
+
+@pytest.mark.parametrize("scale_sign", [1.0, -1.0])
+@pytest.mark.parametrize("dtype", [torch.bfloat16])
+def test_prefill_large_logits(scale_sign, dtype):
+    """Q x 20: logits with a standard deviation of ~20, so exp without the
+    running max overflows fp32; both softmax instances (folded and not)."""
+    announce(f"prefill Q x 20, scale sign {scale_sign}, {dtype}")
+    cfg, inp = make(dtype, 2, 120, 32, 1, 128, seed=8400 + int(scale_sign))
+    inp["Q"] = (inp["Q"].float() * 20).to(dtype)
+    scale = scale_sign * cfg.scale
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], scale)
+    assert_parity(O, ref, dtype, f"prefill Q x 20 scale {scale}")
