@@ -14,7 +14,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
  *     by the caller.  The library allocates nothing and keeps no state beyond
- *     a per-device cache of the compute-unit count.
+ *     a per-device cache of the compute-unit count and the fixed scratch array
+ *     of mqa_decode_noalloc.
  *   - Layouts are dense and row-major; the head dimension d_h is innermost and
  *     contiguous.  Every tensor pointer must be 16-byte aligned.
  *   - q, o, Q, O, k_new, v_new and the cache share one element type
@@ -160,6 +161,27 @@ int mqa_decode_ex(const void* q, const void* k_new, const void* v_new, int32_t h
                   const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
                   int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream,
                   void* ev_begin, void* ev_end);
+
+/* mqa_decode_noalloc -- mqa_decode_ex (k_new / v_new NULL: a plain decode;
+ * non-NULL: the fused append) without a caller workspace and without
+ * allocating anything, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it).
+ * The split-K records live in a fixed array of MQA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per device, held until the process ends; its
+ * address is looked up on the first call on each device.
+ *   Results, arguments and errors as for mqa_decode_ex, plus:
+ *   MQA_ERR_WORKSPACE : the shapes need more than MQA_NOALLOC_SCRATCH_BYTES of
+ *                       records on this device (about 2 * CUs * occupancy
+ *                       records of (h/G) * (d_h + 2) floats, plus 4 * (b + 4)
+ *                       bytes); nothing is launched.
+ *   MQA_ERR_LAUNCH    : the array's address could not be obtained.
+ * Every call on one device shares that array and leaves it as it wrote it:
+ * calls that overlap on one device (concurrent streams, or host threads
+ * without ordering) race and give wrong results.  Order them on one stream. */
+#define MQA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int mqa_decode_noalloc(const void* q, const void* k_new, const void* v_new, int32_t h,
+                       const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                       int32_t window, void* o, void* stream);
 
 /* mqa_prefill_causal -- causal attention over a whole prompt (study notes
  * section 1: O = softmax(Q K^T / sqrt(d_h) + M) V with M_ij = -inf for j > i;

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, minus the ``mqa_`` prefix):
   decode_workspace_size(h, K) / workspace_for(h, K)
   decode(q, K, V, lens, scale, window=0, out=None, workspace=None)
   append_decode(q, k_new, v_new, K, V, lens, scale, ...)   (append fused in)
+  decode_noalloc(q, K, V, lens, scale, ..., k_new=None, v_new=None)
+                                            (no workspace; library scratch)
   prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None)
   check_lens(lens, m_cap)
   strerror(status)
@@ -33,7 +35,8 @@ _DTYPES = {torch.float32: MQA_F32, torch.bfloat16: MQA_BF16}
 
 # Symbols include/mqa.h declares (tests check the library exports each one).
 EXPORTED = ("mqa_kv_append", "mqa_kv_reorder", "mqa_kv_reorder_to", "mqa_decode_workspace_size",
-            "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_prefill_causal", "mqa_attend",
+            "mqa_decode", "mqa_append_decode", "mqa_decode_ex", "mqa_decode_noalloc",
+            "mqa_prefill_causal", "mqa_attend",
             "mqa_check_lens", "mqa_read_probe", "mqa_strerror", "mqa_abi_version")
 
 
@@ -67,6 +70,7 @@ def _load():
         "mqa_decode": ([P, I32, CP, P, F, I32, P, P, SZ, P], ctypes.c_int),
         "mqa_append_decode": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P], ctypes.c_int),
         "mqa_decode_ex": ([P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P], ctypes.c_int),
+        "mqa_decode_noalloc": ([P, P, P, I32, CP, P, P, F, I32, P, P], ctypes.c_int),
         "mqa_prefill_causal": ([P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P],
                                ctypes.c_int),
         "mqa_attend": ([P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, ctypes.c_int64,
@@ -271,6 +275,34 @@ def append_decode(q, k_new, v_new, K, V, lens, scale, window=0, out=None, worksp
         raise ValueError("append_decode needs k_new and v_new")
     return _decode_call(q, k_new, v_new, K, V, lens, scale, window, out, workspace, err_flag,
                         events)
+
+
+def decode_noalloc(q, K, V, lens, scale, window=0, out=None, k_new=None, v_new=None,
+                   err_flag=None):
+    """decode (k_new / v_new None) or append_decode through mqa_decode_noalloc:
+    no workspace argument and no allocation by the library; the split-K
+    records use the library's fixed per-device scratch array, so calls on one
+    device must be ordered (one stream).  ``out`` is allocated here when None;
+    pass it to allocate nothing at all."""
+    if out is None:
+        out = torch.empty_like(q)
+    dev = _dev(q, k_new, v_new, K, V, lens, out, err_flag)
+    b, m_cap, G, dh = K.shape
+    if q.dim() != 3 or q.shape[0] != b or q.shape[2] != dh:
+        raise ValueError("q must be [b, h, d_h] matching the cache")
+    if q.dtype != K.dtype or out.dtype != K.dtype or out.shape != q.shape:
+        raise ValueError("q / out must match the cache dtype and q's shape")
+    if lens.dtype != torch.int32 or lens.shape != (b,):
+        raise ValueError("lens must be int32 [b]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _check_new_rows(k_new, v_new, K, lens)
+    c = _cache(K, V)
+    _check("mqa_decode_noalloc", _lib.mqa_decode_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), q.shape[1], ctypes.byref(c), _ptr(lens),
+        _ptr(err_flag), float(scale), int(window), _ptr(out), _stream(dev)))
+    return out
 
 
 def prefill_causal(Q, K, V, scale, cache_K=None, cache_V=None, lens=None, out=None):

@@ -36,6 +36,9 @@ int current_device_cus(int* device_out) {
 
 namespace {
 
+static_assert(MQA_NOALLOC_SCRATCH_BYTES == mqa::kNoAllocScratchBytes,
+              "the header states the library's scratch size");
+
 constexpr int kMaxHeadsPerGroup = 32;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -100,7 +103,7 @@ int kv_reorder(const mqa_cache* cache, int32_t* lens, int32_t* lens_out, bool ou
 
 extern "C" {
 
-int mqa_abi_version(void) { return 204; }
+int mqa_abi_version(void) { return 205; }
 
 const char* mqa_strerror(int status) {
   switch (status) {
@@ -154,42 +157,82 @@ size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache) {
   return mqa::decode_workspace_bytes(cache->b, h, cache->G, cache->d_h, cache->m_cap);
 }
 
-int mqa_decode_ex(const void* q, const void* k_new, const void* v_new, int32_t h,
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points (everything but the workspace)
+// and the launch parameters; *skip is set when there is nothing to launch.
+int decode_params(const void* q, const void* k_new, const void* v_new, int32_t h,
                   const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
-                  int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream,
-                  void* ev_begin, void* ev_end) {
+                  int32_t window, void* o, mqa::DecodeParams* p, bool* skip) {
+  *skip = false;
   int rc = check_cache(cache);
   if (rc != MQA_OK) return rc;
   rc = check_heads(h, cache->G);
   if (rc != MQA_OK) return rc;
   if (window < 0) return MQA_ERR_SHAPE;
   if ((k_new == nullptr) != (v_new == nullptr)) return MQA_ERR_NULL;
-  if (cache->b == 0) return MQA_OK;
+  if (cache->b == 0) {
+    *skip = true;
+    return MQA_OK;
+  }
   if (!q || !o || !lens) return MQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return MQA_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return MQA_ERR_ALIGN;
+  p->q = q;
+  p->k = cache->k;
+  p->v = cache->v;
+  p->lens = lens;
+  p->k_new = k_new;
+  p->v_new = v_new;
+  p->err_flag = err_flag;
+  p->o = o;
+  p->ws = nullptr;
+  p->b = cache->b;
+  p->h = h;
+  p->G = cache->G;
+  p->dh = cache->d_h;
+  p->m_cap = cache->m_cap;
+  p->window = window;
+  p->dtype = cache->dtype;
+  p->scale = scale;
+  return MQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_decode_ex(const void* q, const void* k_new, const void* v_new, int32_t h,
+                  const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                  int32_t window, void* o, void* workspace, size_t ws_bytes, void* stream,
+                  void* ev_begin, void* ev_end) {
+  mqa::DecodeParams p;
+  bool skip = false;
+  int rc = decode_params(q, k_new, v_new, h, cache, lens, err_flag, scale, window, o, &p, &skip);
+  if (rc != MQA_OK || skip) return rc;
   const size_t need = mqa::decode_workspace_bytes(cache->b, h, cache->G, cache->d_h, cache->m_cap);
   if (!workspace || !aligned16(workspace) || ws_bytes < need) return MQA_ERR_WORKSPACE;
-  mqa::DecodeParams p;
-  p.q = q;
-  p.k = cache->k;
-  p.v = cache->v;
-  p.lens = lens;
-  p.k_new = k_new;
-  p.v_new = v_new;
-  p.err_flag = err_flag;
-  p.o = o;
   p.ws = workspace;
-  p.b = cache->b;
-  p.h = h;
-  p.G = cache->G;
-  p.dh = cache->d_h;
-  p.m_cap = cache->m_cap;
-  p.window = window;
-  p.dtype = cache->dtype;
-  p.scale = scale;
   p.ev_begin = static_cast<hipEvent_t>(ev_begin);
   p.ev_end = static_cast<hipEvent_t>(ev_end);
+  return launch_status(mqa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int mqa_decode_noalloc(const void* q, const void* k_new, const void* v_new, int32_t h,
+                       const mqa_cache* cache, int32_t* lens, int32_t* err_flag, float scale,
+                       int32_t window, void* o, void* stream) {
+  mqa::DecodeParams p;
+  bool skip = false;
+  int rc = decode_params(q, k_new, v_new, h, cache, lens, err_flag, scale, window, o, &p, &skip);
+  if (rc != MQA_OK || skip) return rc;
+  size_t need = 0;
+  if (mqa::decode_launch_workspace_bytes(p, &need) != hipSuccess) return MQA_ERR_LAUNCH;
+  if (need > mqa::kNoAllocScratchBytes) return MQA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (mqa::noalloc_scratch(&ws) != hipSuccess) return MQA_ERR_LAUNCH;
+  p.ws = ws;
   return launch_status(mqa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -57,6 +57,8 @@
 // Each K/V byte is read from HBM once and used by every head of its group.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "mqa_device.h"
 #include "mqa_internal.h"
 
@@ -1115,8 +1117,10 @@ constexpr int kDecodeWaves = 8;
 // many CUs (a CU streams only ~20 GB/s).
 constexpr int kCombineThreads = 128;
 
+// Workgroups of the decode launch for these shapes on the current device:
+// CUs x occupancy, cut to the largest grid the shapes can use.
 template <typename T, int DH>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+hipError_t decode_grid_t(const DecodeParams& p, int* grid_out) {
   auto kern = decode_kernel<T, DH, kDecodeWaves>;
   int dev = 0;
   const int cus = current_device_cus(&dev);
@@ -1139,6 +1143,24 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   const int cap = decode_grid_cap(p.b, p.G, p.m_cap);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
+  *grid_out = grid;
+  return hipSuccess;
+}
+
+hipError_t decode_grid(const DecodeParams& p, int* grid) {
+  if (p.dtype == 1) {
+    if (p.dh == 128) return decode_grid_t<__bf16, 128>(p, grid);
+    return decode_grid_t<__bf16, 64>(p, grid);
+  }
+  if (p.dh == 128) return decode_grid_t<float, 128>(p, grid);
+  return decode_grid_t<float, 64>(p, grid);
+}
+
+template <typename T, int DH>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+  auto kern = decode_kernel<T, DH, kDecodeWaves>;
+  int grid = 0;
+  if (hipError_t e = decode_grid_t<T, DH>(p, &grid); e != hipSuccess) return e;
 
   DecodeArgs a;
   a.q = (const char*)p.q;
@@ -1188,6 +1210,36 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t decode_launch_workspace_bytes(const DecodeParams& p, size_t* bytes) {
+  int grid = 0;
+  if (hipError_t e = decode_grid(p, &grid); e != hipSuccess) return e;
+  const int hg = p.h / p.G;
+  *bytes = decode_records_offset(p.b) + 2 * (size_t)grid * decode_record_bytes(hg, p.dh);
+  return hipSuccess;
+}
+
+// The fixed workspace of the decode variant that allocates nothing.  Host
+// code never passes this name to a kernel (on the host it only stands in for
+// the symbol): it passes the device address that noalloc_scratch looked up.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (p.dtype == 1) {

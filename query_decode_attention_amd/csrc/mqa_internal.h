@@ -64,6 +64,16 @@ size_t decode_records_offset(int b);
 int decode_grid_cap(int b, int G, int m_cap);
 // Workspace bytes for mqa_decode.
 size_t decode_workspace_bytes(int b, int h, int G, int dh, int m_cap);
+// Workspace bytes that the decode launched for p on the current device
+// actually touches (its header and the records of its real grid), at most
+// decode_workspace_bytes of the same shapes.
+hipError_t decode_launch_workspace_bytes(const DecodeParams& p, size_t* bytes);
+
+// The decode workspace of mqa_decode_noalloc: a device array of fixed size
+// in the library itself, one per device, shared by every such call on it.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// Device address of the current device's copy (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

@@ -39,6 +39,7 @@ def lib(libmqa_path):
     L.mqa_decode.argtypes = [P, I32, CP, P, F, I32, P, P, SZ, P]
     L.mqa_append_decode.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P]
     L.mqa_decode_ex.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P, SZ, P, P, P]
+    L.mqa_decode_noalloc.argtypes = [P, P, P, I32, CP, P, P, F, I32, P, P]
     L.mqa_prefill_causal.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, F, CP, P, P, P]
     L.mqa_check_lens.argtypes = [P, I32, I32, P]
     L.mqa_kv_reorder.argtypes = [CP, P, P, I32, P, P]
@@ -61,7 +62,7 @@ def cache(b=2, m_cap=64, G=1, dh=128, dtype=1, k=FAKE, v=FAKE):
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "mqa_abi_version", "mqa_append_decode", "mqa_check_lens", "mqa_decode",
-        "mqa_decode_ex", "mqa_decode_workspace_size",
+        "mqa_decode_ex", "mqa_decode_noalloc", "mqa_decode_workspace_size",
         "mqa_attend", "mqa_kv_append", "mqa_kv_reorder", "mqa_kv_reorder_to", "mqa_prefill_causal",
         "mqa_read_probe",
         "mqa_strerror"])
@@ -80,7 +81,7 @@ def test_library_exports_every_declared_symbol(lib, libmqa_path):
 
 def test_strerror_and_version(lib):
     import query_decode_attention_amd as q
-    assert q.abi_version() == 204
+    assert q.abi_version() == 205
     for code in (OK, ENULL, ESHAPE, EDHEAD, EALIGN, EWS, ELAUNCH, EDTYPE, ELENS):
         assert q.strerror(code) and q.strerror(code) != "unknown status"
     assert q.strerror(12345) == "unknown status"
@@ -146,6 +147,28 @@ def test_fused_append_decode_rejects_bad_arguments(lib):
     # exactly one of k_new / v_new given
     assert ex(FAKE, FAKE, None, 4, ctypes.byref(c), FAKE, None, 1.0, 0, FAKE, FAKE, ws, None,
               None, None) == ENULL
+
+
+def test_noalloc_decode_rejects_bad_arguments_before_any_hip_call(lib):
+    f = lib.mqa_decode_noalloc
+
+    def call(h=4, c=None, q=FAKE, kn=None, vn=None, lens=FAKE, o=FAKE, window=0):
+        c = c if c is not None else cache()
+        return f(q, kn, vn, h, ctypes.byref(c), lens, None, 1.0, window, o, None)
+
+    assert f(FAKE, None, None, 4, None, FAKE, None, 1.0, 0, FAKE, None) == ENULL
+    assert call(q=None) == ENULL
+    assert call(o=None) == ENULL
+    assert call(lens=None) == ENULL
+    assert call(kn=FAKE) == ENULL                       # k_new without v_new
+    assert call(h=3, c=cache(G=2)) == ESHAPE
+    assert call(h=33) == ESHAPE
+    assert call(window=-1) == ESHAPE
+    assert call(c=cache(dh=96)) == EDHEAD
+    assert call(c=cache(dtype=5)) == EDTYPE
+    assert call(o=FAKE_MIS) == EALIGN
+    assert call(kn=FAKE, vn=FAKE_MIS) == EALIGN
+    assert call(c=cache(b=0)) == OK                     # nothing to do, nothing launched
 
 
 def test_append_and_prefill_reject_bad_arguments(lib):
