@@ -19,6 +19,8 @@
 // MFMA) are staged in LDS once and read by all NW waves; LDS is double
 // buffered so the next tile's global loads overlap this tile's MFMAs.  Row
 // blocks are launched last-row-first so the longest causal rows start early.
+#include <type_traits>
+
 #include "mqa_device.h"
 #include "mqa_internal.h"
 #include "mqa_attend.h"
@@ -41,8 +43,11 @@ struct PrefillArgs {
 // MASK (non-causal only): kMaskNone, kMaskKeys (one value per key: the
 // head and query strides are 0, as for key padding) or kMaskFull.
 constexpr int kMaskNone = 0, kMaskKeys = 1, kMaskFull = 2;
+// (Not inlined: the bf16 kernel calls it only to recompute a workgroup whose
+// logits outgrew their fixed softmax reference, and inlining it there would
+// add its registers to the bf16 kernel's hot loops.)
 template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+__device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
   static_assert(NW >= ND, "a wave per d block transposes V");
@@ -230,6 +235,333 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+  prefill_rows<T, DH, NW, CAUSAL, FOLD, MASK>(a);
+}
+
+// ------------------------------------------------------------ bf16 kernel
+//
+// The bf16 path runs the same computation with the tiles of a wave software
+// pipelined, so that matrix-core and vector work overlap inside each wave:
+// iteration j of a wave issues
+//     PV(j-1):  O^T += V_{j-1}^T . P_{j-1}^T     (MFMA)
+//     softmax(j): S_j -> P_j                      (VALU: max, exp2, bf16 pack)
+//     S(j+1) = K_{j+1} . Q^T                      (MFMA)
+// and neither product depends on the softmax between them, so the scheduler
+// is asked to interleave them.  Four LDS buffers: iteration j stages tile
+// j+1 into the buffer of tile j-3, whose last reader (PV of j-3) ran in
+// iteration j-2, so the barrier of iteration j-1 separates every read of a
+// buffer from its next write.  Tiles that every wave of the workgroup sees in
+// full run in a loop without any masking; the diagonal and the tiles after
+// it run in a second loop whose softmax masks by position.
+//
+// The softmax packs its probabilities two at a time (v_cvt_pk_bf16_f32) and
+// sums the packed, rounded values with v_dot2_f32_bf16 against (1, 1), so the
+// normaliser l sums exactly the weights the PV product uses.
+//
+// A column's softmax reference m is fixed at the first tile where it sees a
+// finite logit and is never raised inside the loops: rescaling O under a
+// branch makes the compiler copy the 64 accumulator registers around it,
+// which costs more than the whole softmax.  While no later logit exceeds m
+// by more than kFixedSlack (log2 units), every probability is below
+// 2^kFixedSlack, so l <= n * 2^64 and O stay far inside fp32 and bf16 range.
+// A workgroup in which some column's logit does exceed its reference by more
+// than that recomputes its rows with the rescaling kernel body instead.
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kFixedSlack = 64.0f;
+
+// Softmax of one tile against the column's fixed reference; `over` is set in
+// a lane whose tile maximum exceeds the reference by more than the slack.
+template <int ND, bool FULL, bool BIAS, bool FOLD>
+__device__ __forceinline__ void softmax_fixed(WaveState<ND>& st, const f32x16& s, float scale_log2,
+                                              int pos0, int lim, int half, bf16x8 (&pb)[2],
+                                              const float* bias, bool& over) {
+  static_assert(!(FOLD && BIAS), "the folded form has no bias");
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    x[r] = FOLD ? s[r] : s[r] * scale_log2;
+    if constexpr (BIAS) x[r] += bias[r];
+    if (!FULL && pos0 + d_row(r, half) > lim) x[r] = kNegInf;
+  }
+  // max over the lane's 16 values in a tree of three-input maxima
+  float m3[6];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
+  m3[5] = x[15];
+  float mt = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
+  mt = fmaxf(fmaxf(mt, m3[3]), fmaxf(m3[4], m3[5]));
+  mt = max_halves(mt);
+  if constexpr (FOLD) mt *= scale_log2;  // -inf stays -inf (scale_log2 > 0)
+  over = over || (st.m != kNegInf && mt > st.m + kFixedSlack);
+  st.m = (st.m == kNegInf) ? mt : st.m;
+  const float ref = (st.m == kNegInf) ? 0.f : st.m;
+  bf16x2 p2[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float e0 = fast_exp2(FOLD ? __builtin_fmaf(x[2 * k], scale_log2, -ref) : x[2 * k] - ref);
+    const float e1 =
+        fast_exp2(FOLD ? __builtin_fmaf(x[2 * k + 1], scale_log2, -ref) : x[2 * k + 1] - ref);
+    p2[k] = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float sa = 0.f, sb = 0.f;  // two chains of dependent sums
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    sa = __builtin_amdgcn_fdot2_f32_bf16(p2[k], ones, sa, false);
+    sb = __builtin_amdgcn_fdot2_f32_bf16(p2[k + 1], ones, sb, false);
+  }
+  st.l += sa + sb;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pb[h] = bf16x8{p2[4 * h][0], p2[4 * h][1], p2[4 * h + 1][0], p2[4 * h + 1][1],
+                   p2[4 * h + 2][0], p2[4 * h + 2][1], p2[4 * h + 3][0], p2[4 * h + 3][1]};
+  }
+}
+
+template <int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
+  using T = __bf16;
+  using S = TileShape<T, DH>;
+  constexpr int NQ = S::NQ, ND = S::ND;
+  constexpr int NB = 4;                       // LDS tile buffers (a power of two)
+  constexpr int VPW = NQ / ND;                // V chunks per d block (2)
+  constexpr int KPW = (NQ + NW - 1) / NW;     // K chunks staged per wave
+  static_assert(NW >= ND, "a wave per d block transposes V");
+  constexpr bool BIAS = MASK != kMaskNone;
+  __shared__ u32x4 s_k[NB][NQ][64];
+  __shared__ u32x4 s_vt[NB][ND][2][64];
+  __shared__ f32x4 s_kb[NB][kTileRows / 4];  // per-key mask of the tile (key padding)
+  __shared__ int s_over;                     // some column exceeded its reference
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+
+  const int rb = a.nrb - 1 - (int)(blockIdx.x % a.nrb);
+  const int bg = blockIdx.x / a.nrb;
+  const int bi = bg / a.G, g = bg % a.G;
+  const int rows_per_block = NW * a.rpw;
+  const int r_begin = rb * rows_per_block;
+  if (r_begin >= a.n) return;
+  const int r_end = min(a.n, r_begin + rows_per_block);
+  const int ntiles = CAUSAL ? (r_end - 1) / kTileRows + 1 : (a.m + kTileRows - 1) / kTileRows;
+  // tiles [0, j_full) are visible in full to every column of the workgroup
+  const int j_full = CAUSAL ? (r_begin + 1) / kTileRows : a.m / kTileRows;
+
+  const int w_row0 = r_begin + wave * a.rpw;
+  const int w_last = min(a.n - 1, w_row0 + a.rpw - 1);
+  const int w_tiles = (w_row0 < a.n) ? (CAUSAL ? w_last / kTileRows + 1 : ntiles) : 0;
+  const int crow = w_row0 + col / a.hgp;
+  const int chead = col % a.hgp;
+  const bool col_ok = crow < a.n && chead < a.hg;
+  const int lim = CAUSAL ? crow : a.m - 1;
+  if (threadIdx.x == 0) s_over = 0;  // ordered before its readers by the loops' barriers
+
+  u32x4 qr[NQ];
+  {
+    // columns past n or past h/G read a real row (finite values, never stored)
+    const int qrow = crow < a.n ? crow : a.n - 1;
+    const int qhead = chead < a.hg ? chead : 0;
+    const char* qp =
+        a.Q + (((size_t)bi * a.n + qrow) * a.h + (size_t)g * a.hg + qhead) * DH * sizeof(T);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) qr[c] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
+  }
+
+  SelOps<T> sel;
+  sel.init(col, half);
+  const size_t rs = (size_t)a.G * DH * sizeof(T);
+  const size_t seq_off = ((size_t)bi * a.m * a.G + (size_t)g) * DH * sizeof(T);
+  const char* kseq = a.K + seq_off;
+  const char* vseq = a.V + seq_off;
+
+  // Staging, one tile ahead: wave w loads K chunks w, w + NW, ...; waves
+  // below ND load and transpose d block `wave` of V; with a key-padding mask
+  // the last wave loads the tile's 32 values.  Positions past m read row
+  // m - 1 (finite; masked).
+  const bool v_wave = wave < ND;
+  const bool kb_wave = MASK == kMaskKeys && wave == NW - 1;
+  const float* kb_row = kb_wave ? a.mask + (int64_t)bi * a.msb : nullptr;
+  struct Chunks {
+    u32x4 k[KPW];
+    u32x4 v[VPW];
+    float kb;
+  };
+  auto issue = [&](int tile, Chunks& ld) {
+    const int pos0 = tile * kTileRows + col;
+    const int pos = pos0 < a.m ? pos0 : a.m - 1;
+    const char* kp = kseq + (size_t)pos * rs;
+    const char* vp = vseq + (size_t)pos * rs;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int c = wave + i * NW;
+      if (c < NQ) ld.k[i] = *reinterpret_cast<const u32x4*>(kp + (2 * c + half) * 16);
+    }
+    if (v_wave) {
+#pragma unroll
+      for (int i = 0; i < VPW; ++i)
+        ld.v[i] = *reinterpret_cast<const u32x4*>(vp + (2 * (wave * VPW + i) + half) * 16);
+    }
+    if (kb_wave) ld.kb = kb_row[pos] * 1.4426950408889634f;  // log2 units
+  };
+  auto commit = [&](int buf, const Chunks& ld) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int c = wave + i * NW;
+      if (c < NQ) s_k[buf][c][lane] = ld.k[i];
+    }
+    if (v_wave) {
+      u32x4 ops[2];
+      transpose_block<T, VPW>(ld.v, 0, sel, ops);
+      s_vt[buf][wave][0][lane] = ops[0];
+      s_vt[buf][wave][1][lane] = ops[1];
+    }
+    if (kb_wave && half == 0) reinterpret_cast<float*>(s_kb[buf])[col] = ld.kb;
+  };
+
+  // additive mask row of this lane's column (general mask only)
+  const float* mrow = nullptr;
+  if (MASK == kMaskFull && col_ok)
+    mrow = a.mask + (int64_t)bi * a.msb + (int64_t)(g * a.hg + chead) * a.msh + (int64_t)crow * a.msn;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  WaveState<ND> st;
+  st.reset();
+  f32x16 s_cur = {};   // S_j
+  bf16x8 p_prev[2];    // P_{j-1}
+  p_prev[0] = p_prev[1] = bf16x8{};
+  bool over = false;
+
+  auto scores = [&](int buf, const f32x16& init) {
+    u32x4 kr[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
+    f32x16 s = init;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) s = mfma_bf16(as_bf16x8(kr[c]), as_bf16x8(qr[c]), s);
+    return s;
+  };
+  auto pv = [&](int buf) {
+    u32x4 vr[ND][2];
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) vr[d][k] = s_vt[buf][d][k][lane];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      st.o[d] = mfma_bf16(as_bf16x8(vr[d][0]), p_prev[0], st.o[d]);
+      st.o[d] = mfma_bf16(as_bf16x8(vr[d][1]), p_prev[1], st.o[d]);
+    }
+  };
+  // Mask values of tile j, register r holding key d_row(r, half), in log2
+  // units (masked kinds only).
+  auto load_bias = [&](int j, float (&bias)[16]) {
+    if constexpr (MASK == kMaskKeys) {
+      // keys 8k + 4*half .. +3 of the tile for registers 4k .. 4k+3
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 kb = s_kb[j & (NB - 1)][2 * k + half];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e];
+      }
+    } else if constexpr (MASK == kMaskFull) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = j * kTileRows + d_row(r, half);
+        bias[r] = (mrow && jj < a.m) ? mrow[jj] * kLog2e : 0.f;
+      }
+    }
+  };
+  // The initial accumulator of tile j's score product.  With a positive
+  // scale c (log2 units) the mask enters here as mask / c, so that the
+  // folded softmax's c * (s + mask / c) is the masked logit; otherwise the
+  // product starts from zero and the softmax adds the mask.
+  const float inv_c = FOLD ? 1.0f / a.scale_log2 : 0.f;
+  auto score_init = [&](int j) {
+    f32x16 init = {};
+    if constexpr (FOLD && BIAS) {
+      float b[16];
+      load_bias(j, b);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) init[r] = b[r] * inv_c;
+    }
+    return init;
+  };
+  constexpr bool SM_BIAS = BIAS && !FOLD;  // the softmax adds the mask itself
+
+  // One iteration.  Every iteration runs both products and the softmax (a
+  // product under a branch makes the compiler copy the accumulators): a tile
+  // past the wave's last goes through the masked softmax with every key
+  // hidden, which leaves (m, l, O) unchanged and yields P = 0, so the next PV
+  // adds exactly zero; the score product of a tile no one will read is
+  // discarded the same way.
+  Chunks ld;
+  auto iter = [&](int j, auto full_tile) {
+    constexpr bool FULL = decltype(full_tile)::value;
+    if (j + 1 < ntiles) {
+      commit((j + 1) & (NB - 1), ld);
+      if (j + 2 < ntiles) issue(j + 2, ld);
+    }
+    __syncthreads();
+    // PV of tile j - 1 (tile 0's buffer when j = 0: finite, and P = 0)
+    pv(j == 0 ? 0 : (j - 1) & (NB - 1));
+    float bias[16];
+    if constexpr (SM_BIAS) load_bias(j, bias);
+    bf16x8 p_cur[2];
+    softmax_fixed<ND, FULL, SM_BIAS, FOLD>(st, s_cur, a.scale_log2, j * kTileRows,
+                                           j < w_tiles ? lim : -1, half, p_cur, bias, over);
+    s_cur = scores((j + 1) & (NB - 1), score_init(j + 1));
+    p_prev[0] = p_cur[0];
+    p_prev[1] = p_cur[1];
+    if constexpr (FULL) {
+      // the LDS operands first, then the MFMAs spread over the vector work
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * ND + NQ, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * ND + NQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
+  };
+
+  // prologue: tile 0 staged and its scores computed, tile 1 loaded
+  issue(0, ld);
+  commit(0, ld);
+  if (ntiles > 1) issue(1, ld);
+  __syncthreads();
+  s_cur = scores(0, score_init(0));
+  int j = 0;
+  for (; j < j_full; ++j) iter(j, std::true_type{});
+  for (; j <= ntiles; ++j) iter(j, std::false_type{});
+
+  if (__any(over) && lane == 0) s_over = 1;
+  __syncthreads();
+  if (s_over) {
+    // some logit exceeded its column's fixed reference by more than the
+    // slack: recompute the workgroup's rows with the rescaling kernel body
+    prefill_rows<T, DH, NW, CAUSAL, false, MASK>(a);
+    return;
+  }
+
+  const float l_tot = sum_halves(st.l);
+  if (col_ok) {
+    // a row whose every key is masked out gets zeros (as an empty decode row)
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    T* op = reinterpret_cast<T*>(a.O) + (((size_t)bi * a.n + crow) * a.h + (size_t)g * a.hg + chead) * DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store4(op + 32 * d + 8 * r4 + 4 * half, st.o[d][4 * r4] * inv, st.o[d][4 * r4 + 1] * inv,
+               st.o[d][4 * r4 + 2] * inv, st.o[d][4 * r4 + 3] * inv);
+  }
+}
+
 // Copies the prompt's K/V rows into positions [0, n) of every sequence of the
 // cache and sets lens[b] = n.
 __global__ void prefill_cache_copy_kernel(const char* K, const char* V, char* ck, char* cv,
@@ -277,6 +609,18 @@ PrefillArgs row_blocks(const PrefillParams& p, int m) {
   return a;
 }
 
+// The kernel for element type T: the pipelined one for bf16, the plain one
+// (fp32 operands twice as wide) otherwise.
+template <typename T, int DH, bool CAUSAL, bool FOLD, int MASK>
+void launch_rows(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((prefill_bf16_kernel<DH, kPrefillWaves, CAUSAL, FOLD, MASK>), grid,
+                       dim3(kPrefillWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, CAUSAL, FOLD, MASK>), grid,
+                       dim3(kPrefillWaves * 64), 0, s, a);
+}
+
 template <typename T, int DH>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   const int row_bytes = p.G * p.dh * (int)sizeof(T);
@@ -293,13 +637,11 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const PrefillArgs a = row_blocks(p, p.n);
-  const size_t blocks = (size_t)p.b * p.G * a.nrb;
+  const dim3 grid((unsigned)((size_t)p.b * p.G * a.nrb));
   if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, true, kMaskNone>),
-                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
+    launch_rows<T, DH, true, true, kMaskNone>(a, grid, s);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, true, false, kMaskNone>),
-                       dim3((unsigned)blocks), dim3(kPrefillWaves * 64), 0, s, a);
+    launch_rows<T, DH, true, false, kMaskNone>(a, grid, s);
   return hipGetLastError();
 }
 
@@ -310,20 +652,25 @@ hipError_t launch_attend_t(const AttendParams& q, hipStream_t s) {
   a.msb = q.msb;
   a.msh = q.msh;
   a.msn = q.msn;
-  const size_t blocks = (size_t)q.base.b * q.base.G * a.nrb;
-  const dim3 grid((unsigned)blocks), block(kPrefillWaves * 64);
-  if (q.mask && q.msh == 0 && q.msn == 0)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskKeys>), grid,
-                       block, 0, s, a);
-  else if (q.mask)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskFull>), grid,
-                       block, 0, s, a);
-  else if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, true, kMaskNone>), grid,
-                       block, 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, false, false, kMaskNone>), grid,
-                       block, 0, s, a);
+  const dim3 grid((unsigned)((size_t)q.base.b * q.base.G * a.nrb));
+  const bool fold = a.scale_log2 > 0.f;
+  const int kind = !q.mask ? kMaskNone : (q.msh == 0 && q.msn == 0) ? kMaskKeys : kMaskFull;
+  if (kind == kMaskNone) {
+    if (fold) launch_rows<T, DH, false, true, kMaskNone>(a, grid, s);
+    else launch_rows<T, DH, false, false, kMaskNone>(a, grid, s);
+  } else if constexpr (sizeof(T) == 2) {
+    // bf16: a positive scale folds the mask into the score product too
+    if (kind == kMaskKeys) {
+      if (fold) launch_rows<T, DH, false, true, kMaskKeys>(a, grid, s);
+      else launch_rows<T, DH, false, false, kMaskKeys>(a, grid, s);
+    } else {
+      if (fold) launch_rows<T, DH, false, true, kMaskFull>(a, grid, s);
+      else launch_rows<T, DH, false, false, kMaskFull>(a, grid, s);
+    }
+  } else {
+    if (kind == kMaskKeys) launch_rows<T, DH, false, false, kMaskKeys>(a, grid, s);
+    else launch_rows<T, DH, false, false, kMaskFull>(a, grid, s);
+  }
   return hipGetLastError();
 }
 }  // namespace

@@ -158,3 +158,25 @@ def test_attend_large_logits(kind, scale_sign):
     torch.cuda.synchronize()
     ref = oracle_ref(inp["Q"], inp["K"], inp["V"], scale, mask)
     assert_parity(out, ref, torch.bfloat16, what)
+
+
+@pytest.mark.parametrize("kind", ["none", "pad", "full"])
+def test_attend_logit_jump_past_the_reference(kind):
+    """A key whose logit exceeds the first tile's maximum by far more than
+    the bf16 kernel's fixed-reference slack (key 100 of 300, logit ~70.7):
+    every workgroup takes the rescaling path, with each mask kind."""
+    b, n, m, h, G, dh = 2, 19, 300, 32, 1, 128
+    what = f"attend logit jump mask={kind}"
+    announce(what)
+    cfg = W.MemoryConfig("t", torch.bfloat16, b, n, m, h, G, dh, m, m, 440 + len(kind))
+    inp = W.memory_inputs(cfg)
+    inp["Q"][..., 0] = 20.0
+    inp["K"][:, 100, :, 0] = 40.0
+    mask = make_mask(kind, b, h, n, m, 441)
+    if kind == "pad":
+        mask[..., :150] = 0.0          # key 100 stays visible
+    out = mqa.attend(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale,
+                     mask=None if mask is None else mask.cuda())
+    torch.cuda.synchronize()
+    ref = oracle_ref(inp["Q"], inp["K"], inp["V"], cfg.scale, mask)
+    assert_parity(out, ref, torch.bfloat16, what)

@@ -134,3 +134,21 @@ def test_prefill_large_logits(scale_sign, dtype):
     torch.cuda.synchronize()
     ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], scale)
     assert_parity(O, ref, dtype, f"prefill Q x 20 scale {scale}")
+
+
+@pytest.mark.parametrize("jump_at", [100, 5])
+def test_prefill_logit_jump_past_the_reference(jump_at):
+    """The bf16 kernel fixes each column's softmax reference at its first
+    visible tile; a key whose logit exceeds it by more than the slack sends
+    the workgroup to the rescaling path.  Q[..., 0] = 20 and K[jump_at, 0] =
+    40 give that key a logit of ~70.7 against ~N(0, 1) elsewhere: at key 100
+    (tile 3) the rows that see it take the rescaling path, at key 5 (tile 0)
+    the reference already holds it."""
+    announce(f"prefill logit jump at key {jump_at}")
+    cfg, inp = make(torch.bfloat16, 2, 180, 32, 1, 128, seed=8500 + jump_at)
+    inp["Q"][..., 0] = 20.0
+    inp["K"][:, jump_at, :, 0] = 40.0
+    O = mqa.prefill_causal(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], cfg.scale)
+    assert_parity(O, ref, torch.bfloat16, f"prefill logit jump at key {jump_at}")
