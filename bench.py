@@ -369,8 +369,11 @@ def prefill_result(cfg, trials, torch, mqa, R=2, calls=4):
 
 def attend_result(cfg, trials, torch, mqa, R=2, calls=4):
     """Attention over a fixed memory with a key-padding mask (encoder-decoder
-    attention).  `flops` counts every (query, memory position) pair;
-    `useful_tflops` counts only the pairs the mask leaves visible."""
+    attention).  The kernel stops each sequence after its last 32-key tile
+    with a visible key, so `flops` counts the (query, key) pairs of the tiles
+    it runs (visible keys rounded up to 32); `useful_tflops` counts only the
+    pairs the mask leaves visible, `all_pairs_tflops` every pair of the m
+    positions."""
     dev = torch.device("cuda")
     copies = []
     visible = []
@@ -383,7 +386,8 @@ def attend_result(cfg, trials, torch, mqa, R=2, calls=4):
         mem = torch.randint(cfg.mem_lo, cfg.mem_hi + 1, (cfg.b,), generator=gc)
         mask = torch.where(torch.arange(cfg.m)[None, :] < mem[:, None], 0.0, float("-inf"))
         copies.append((Q, K, V, mask.view(cfg.b, 1, 1, cfg.m).to(dev)))
-        visible.append(int(mem.sum()))
+        visible.append((int(mem.sum()),
+                        int(sum(min(cfg.m, -(-int(v) // 32) * 32) for v in mem))))
     O = torch.empty_like(copies[0][0])
 
     def body():
@@ -395,13 +399,15 @@ def attend_result(cfg, trials, torch, mqa, R=2, calls=4):
     torch.cuda.synchronize()
     secs = event_trials(torch, body, trials)
     dt = median(secs) / calls
-    flops = 4 * cfg.b * cfg.h * cfg.dh * cfg.n * cfg.m
-    useful = sum(4 * cfg.h * cfg.dh * cfg.n * visible[i % R] for i in range(calls)) / calls
+    all_pairs = 4 * cfg.b * cfg.h * cfg.dh * cfg.n * cfg.m
+    useful = sum(4 * cfg.h * cfg.dh * cfg.n * visible[i % R][0] for i in range(calls)) / calls
+    flops = sum(4 * cfg.h * cfg.dh * cfg.n * visible[i % R][1] for i in range(calls)) / calls
     return dict(trials=trials, ms_per_call=dt * 1e3, ms_per_call_min=1e3 * min(secs) / calls,
                 ms_per_call_max=1e3 * max(secs) / calls, tflops=flops / dt / 1e12,
                 mfma_frac_of_peak=flops / dt / 1e12 / BF16_PEAK_TFLOPS, flops=flops,
                 useful_tflops=useful / dt / 1e12,
-                useful_frac_of_peak=useful / dt / 1e12 / BF16_PEAK_TFLOPS)
+                useful_frac_of_peak=useful / dt / 1e12 / BF16_PEAK_TFLOPS,
+                all_pairs_tflops=all_pairs / dt / 1e12)
 
 
 # --------------------------------------------------------------------------- beam

@@ -334,14 +334,6 @@ struct SlotIndex {
   __device__ __forceinline__ int d() const { return 32 * blk + 8 * r4 + 4 * (lane >> 5); }
 };
 
-// 16 bytes per lane from `src` straight into LDS word `lane` of `dst` (the
-// direct-to-LDS load path; the LDS base must be the same for the whole wave).
-// Completion is counted by vmcnt.
-__device__ __forceinline__ void load_to_lds(const char* src, u32x4* dst) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
-                                   16, 0, 0);
-}
-
 // Q^T operand of group g of sequence bi in LDS, lane order: chunk c of lane l
 // is head l % 32, 16-byte chunk 2c + l / 32 of its row.  Columns of heads
 // >= h/G repeat a real head, so they hold finite values; every head column

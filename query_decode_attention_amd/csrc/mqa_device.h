@@ -37,6 +37,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// 16 bytes per lane from `src` straight into LDS word `lane` of `dst` (the
+// direct-to-LDS load path; the LDS base must be the same for the whole wave).
+// Completion is counted by vmcnt.
+__device__ __forceinline__ void load_to_lds(const char* src, u32x4* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
+                                   16, 0, 0);
+}
+
 // Combine a value with the one held by lane ^ 32, through one cross-half
 // swap (v_permlane32_swap: each lane receives the values of lanes l % 32 and
 // l % 32 + 32, in that order, so both halves compute the same result).

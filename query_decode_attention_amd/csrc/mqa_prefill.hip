@@ -268,15 +268,57 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 // 2^kFixedSlack, so l <= n * 2^64 and O stay far inside fp32 and bf16 range.
 // A workgroup in which some column's logit does exceed its reference by more
 // than that recomputes its rows with the rescaling kernel body instead.
+//
+// Once every column of a wave holds its reference, its tiles skip the tile
+// maximum altogether: a probability above 2^kFixedSlack then shows in the
+// lane's sum of the tile's rounded probabilities, which is at least as large
+// (all terms are non-negative, and bf16 rounding to nearest keeps a value
+// above 2^64 at or above 2^64).  The sum test also fires for sums of many
+// smaller terms that reach 2^64; those workgroups take the exact rescue too.
+// Every flag is set branch-free, so a tile's products and softmax stay one
+// basic block the scheduler can interleave.
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Workgroup barrier for LDS data only: this wave's LDS writes complete, then
+// s_barrier.  __syncthreads() would also wait for every outstanding memory
+// load, including direct-to-LDS loads of tiles that are not needed yet;
+// those are waited for by the wave that issued them (s_waitcnt vmcnt)
+// before the barrier that publishes them.  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Largest index p < m with mask[p] != -inf (the last key a key-padding mask
+// leaves visible), or -1; the same in every lane of the wave.
+__device__ __forceinline__ int last_visible_key(const float* mask, int m, int lane) {
+  int last = -1;
+  int p = lane;
+  for (; p + 7 * 64 < m; p += 8 * 64) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = mask[p + u * 64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) last = v[u] != kNegInf ? p + u * 64 : last;
+  }
+  for (; p < m; p += 64) last = mask[p] != kNegInf ? p : last;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  return last;
+}
+
 constexpr float kFixedSlack = 64.0f;
+constexpr float kOverSum = 0x1p64f;  // 2^kFixedSlack
 
 // Softmax of one tile against the column's fixed reference; `over` is set in
-// a lane whose tile maximum exceeds the reference by more than the slack.
-template <int ND, bool FULL, bool BIAS, bool FOLD>
+// a lane whose tile exceeds the reference by more than the slack.  REF: every
+// column of the wave already holds a finite reference (no tile maximum).
+template <int ND, bool FULL, bool BIAS, bool FOLD, bool REF>
 __device__ __forceinline__ void softmax_fixed(WaveState<ND>& st, const f32x16& s, float scale_log2,
                                               int pos0, int lim, int half, bf16x8 (&pb)[2],
                                               const float* bias, bool& over) {
@@ -288,18 +330,22 @@ __device__ __forceinline__ void softmax_fixed(WaveState<ND>& st, const f32x16& s
     if constexpr (BIAS) x[r] += bias[r];
     if (!FULL && pos0 + d_row(r, half) > lim) x[r] = kNegInf;
   }
-  // max over the lane's 16 values in a tree of three-input maxima
-  float m3[6];
+  float ref = st.m;
+  if constexpr (!REF) {
+    // max over the lane's 16 values in a tree of three-input maxima
+    float m3[6];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
-  m3[5] = x[15];
-  float mt = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
-  mt = fmaxf(fmaxf(mt, m3[3]), fmaxf(m3[4], m3[5]));
-  mt = max_halves(mt);
-  if constexpr (FOLD) mt *= scale_log2;  // -inf stays -inf (scale_log2 > 0)
-  over = over || (st.m != kNegInf && mt > st.m + kFixedSlack);
-  st.m = (st.m == kNegInf) ? mt : st.m;
-  const float ref = (st.m == kNegInf) ? 0.f : st.m;
+    for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
+    m3[5] = x[15];
+    float mt = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
+    mt = fmaxf(fmaxf(mt, m3[3]), fmaxf(m3[4], m3[5]));
+    mt = max_halves(mt);
+    if constexpr (FOLD) mt *= scale_log2;  // -inf stays -inf (scale_log2 > 0)
+    const bool had = st.m != kNegInf;
+    over = over | (had & (mt > st.m + kFixedSlack));
+    st.m = had ? st.m : mt;
+    ref = (st.m == kNegInf) ? 0.f : st.m;
+  }
   bf16x2 p2[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -315,7 +361,9 @@ __device__ __forceinline__ void softmax_fixed(WaveState<ND>& st, const f32x16& s
     sa = __builtin_amdgcn_fdot2_f32_bf16(p2[k], ones, sa, false);
     sb = __builtin_amdgcn_fdot2_f32_bf16(p2[k + 1], ones, sb, false);
   }
-  st.l += sa + sb;
+  const float tile_sum = sa + sb;
+  if constexpr (REF) over = over | (tile_sum >= kOverSum);
+  st.l += tile_sum;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     pb[h] = bf16x8{p2[4 * h][0], p2[4 * h][1], p2[4 * h + 1][0], p2[4 * h + 1][1],
@@ -332,10 +380,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int VPW = NQ / ND;                // V chunks per d block (2)
   constexpr int KPW = (NQ + NW - 1) / NW;     // K chunks staged per wave
   static_assert(NW >= ND, "a wave per d block transposes V");
+  static_assert(VPW == 2, "two V chunks per d block");
   constexpr bool BIAS = MASK != kMaskNone;
+  // Staging (a measured choice): causal prefill stages through registers one
+  // tile ahead; attention over a fixed memory loads straight into LDS.
+  constexpr bool DMA = !CAUSAL;
   __shared__ u32x4 s_k[NB][NQ][64];
-  __shared__ u32x4 s_vt[NB][ND][2][64];
+  __shared__ u32x4 s_vt[NB][ND][2][64];      // V transposed: the PV operand
+  __shared__ u32x4 s_vr[NB][NQ][64];         // V rows as loaded (direct staging)
   __shared__ f32x4 s_kb[NB][kTileRows / 4];  // per-key mask of the tile (key padding)
+  __shared__ float s_kbw[NB][NW][64];        // the same, a copy per wave (direct staging)
   __shared__ int s_over;                     // some column exceeded its reference
 
   const int lane = threadIdx.x & 63;
@@ -349,9 +403,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   const int r_begin = rb * rows_per_block;
   if (r_begin >= a.n) return;
   const int r_end = min(a.n, r_begin + rows_per_block);
-  const int ntiles = CAUSAL ? (r_end - 1) / kTileRows + 1 : (a.m + kTileRows - 1) / kTileRows;
+  int ntiles = CAUSAL ? (r_end - 1) / kTileRows + 1 : (a.m + kTileRows - 1) / kTileRows;
+  if constexpr (MASK == kMaskKeys) {
+    // tiles past the last key the mask leaves visible add exactly nothing:
+    // skip them (tile 0 always runs, so a fully hidden row still ends at 0)
+    const int last = last_visible_key(a.mask + (int64_t)bi * a.msb, a.m, lane);
+    ntiles = min(ntiles, max(1, last / kTileRows + 1));
+  }
   // tiles [0, j_full) are visible in full to every column of the workgroup
-  const int j_full = CAUSAL ? (r_begin + 1) / kTileRows : a.m / kTileRows;
+  const int j_full = min(ntiles, CAUSAL ? (r_begin + 1) / kTileRows : a.m / kTileRows);
 
   const int w_row0 = r_begin + wave * a.rpw;
   const int w_last = min(a.n - 1, w_row0 + a.rpw - 1);
@@ -424,6 +484,69 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
     if (kb_wave && half == 0) reinterpret_cast<float*>(s_kb[buf])[col] = ld.kb;
   };
 
+  // Direct-to-LDS staging, three tiles ahead of the iteration that issues
+  // it: the 2*NQ chunks of K and V rows of a tile (1 KB each) are shared out
+  // evenly, wave w taking chunks w, w + NW, ...; with a key-padding mask
+  // every wave also fetches the tile's mask values into a slot of its own.
+  // In iteration t, before its barrier, the waves below ND transpose d
+  // block `wave` of the V rows of tile t + 1 into the PV operand layout.
+  constexpr int CPW = 2 * NQ / NW;  // chunks per wave and tile
+  static_assert(!DMA || 2 * NQ % NW == 0, "K and V chunks shared out evenly");
+  const float* kbw_row = MASK == kMaskKeys ? a.mask + (int64_t)bi * a.msb : nullptr;
+  const uint32_t rs32 = (uint32_t)rs;
+  auto issue_dma = [&](int tile) {
+    const int pos0 = tile * kTileRows + col;
+    const uint32_t pos = (uint32_t)(pos0 < a.m ? pos0 : a.m - 1);
+    const uint64_t off = (uint64_t)pos * rs32;  // one 32 x 32 -> 64-bit multiply
+    const int buf = tile & (NB - 1);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = wave + i * NW;  // wave-uniform
+      if (c < NQ)
+        load_to_lds(kseq + off + (2 * c + half) * 16, &s_k[buf][c][0]);
+      else
+        load_to_lds(vseq + off + (2 * (c - NQ) + half) * 16, &s_vr[buf][c - NQ][0]);
+    }
+    // lanes 32..63 repeat lanes 0..31 into the slot's second half
+    if constexpr (MASK == kMaskKeys)
+      __builtin_amdgcn_global_load_lds((const void*)(kbw_row + pos),
+                                       (__attribute__((address_space(3))) void*)&s_kbw[buf][wave][0],
+                                       4, 0, 0);
+  };
+  auto transpose_v = [&](int t) {
+    const int buf = t & (NB - 1);
+    // The compiler cannot tell these reads from the locations that
+    // direct-to-LDS loads still in flight write, and would wait for all of
+    // them; the rows were published by the issuing waves' waits and a
+    // barrier, so the reads are issued here with a wait of their own.
+    u32x4 vr[VPW];
+    const uint32_t addr = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) u32x4*)&s_vr[buf][wave * VPW][lane]);
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1])
+        : "v"(addr)
+        : "memory");
+    u32x4 ops[2];
+    transpose_block<T, VPW>(vr, 0, sel, ops);
+    s_vt[buf][wave][0][lane] = ops[0];
+    s_vt[buf][wave][1][lane] = ops[1];
+  };
+  // Loads each wave issues per tile.  Tile t has landed once at most the
+  // loads issued after it are outstanding (loads complete in order): those
+  // of tile t + 1, if there is one.
+  constexpr int kPerTile = CPW + (MASK == kMaskKeys ? 1 : 0);
+  static_assert(kPerTile <= 15, "vmcnt immediate");
+  auto wait_tile = [&](int t) {
+    if (t >= ntiles) return;
+    if (t + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+
   // additive mask row of this lane's column (general mask only)
   const float* mrow = nullptr;
   if (MASK == kMaskFull && col_ok)
@@ -465,9 +588,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
       // keys 8k + 4*half .. +3 of the tile for registers 4k .. 4k+3
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x4 kb = s_kb[j & (NB - 1)][2 * k + half];
+        if constexpr (DMA) {
+          const f32x4 kb = reinterpret_cast<const f32x4*>(s_kbw[j & (NB - 1)][wave])[2 * k + half];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e];
+          for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e] * kLog2e;
+        } else {
+          const f32x4 kb = s_kb[j & (NB - 1)][2 * k + half];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e];
+        }
       }
     } else if constexpr (MASK == kMaskFull) {
 #pragma unroll
@@ -501,19 +630,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   // adds exactly zero; the score product of a tile no one will read is
   // discarded the same way.
   Chunks ld;
-  auto iter = [&](int j, auto full_tile) {
+  auto iter = [&](int j, auto full_tile, auto ref_known) {
     constexpr bool FULL = decltype(full_tile)::value;
-    if (j + 1 < ntiles) {
-      commit((j + 1) & (NB - 1), ld);
-      if (j + 2 < ntiles) issue(j + 2, ld);
+    constexpr bool REF = decltype(ref_known)::value;
+    if constexpr (DMA) {
+      if (j + 3 < ntiles) issue_dma(j + 3);
+      if (v_wave && j + 1 < ntiles) transpose_v(j + 1);
+      wait_tile(j + 2);
+      lds_barrier();
+    } else {
+      if (j + 1 < ntiles) {
+        commit((j + 1) & (NB - 1), ld);
+        if (j + 2 < ntiles) issue(j + 2, ld);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // PV of tile j - 1 (tile 0's buffer when j = 0: finite, and P = 0)
     pv(j == 0 ? 0 : (j - 1) & (NB - 1));
     float bias[16];
     if constexpr (SM_BIAS) load_bias(j, bias);
     bf16x8 p_cur[2];
-    softmax_fixed<ND, FULL, SM_BIAS, FOLD>(st, s_cur, a.scale_log2, j * kTileRows,
+    softmax_fixed<ND, FULL, SM_BIAS, FOLD, REF>(st, s_cur, a.scale_log2, j * kTileRows,
                                            j < w_tiles ? lim : -1, half, p_cur, bias, over);
     s_cur = scores((j + 1) & (NB - 1), score_init(j + 1));
     p_prev[0] = p_cur[0];
@@ -530,14 +667,33 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   };
 
   // prologue: tile 0 staged and its scores computed, tile 1 loaded
-  issue(0, ld);
-  commit(0, ld);
-  if (ntiles > 1) issue(1, ld);
-  __syncthreads();
+  if constexpr (DMA) {
+    // tiles 0, 1 and 2 in flight; 0 and 1 landed and published, 0 transposed
+    issue_dma(0);
+    if (ntiles > 1) issue_dma(1);
+    if (ntiles > 2) issue_dma(2);
+    if (ntiles > 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+    if (v_wave) transpose_v(0);
+  } else {
+    issue(0, ld);
+    commit(0, ld);
+    if (ntiles > 1) issue(1, ld);
+    __syncthreads();
+  }
   s_cur = scores(0, score_init(0));
-  int j = 0;
-  for (; j < j_full; ++j) iter(j, std::true_type{});
-  for (; j <= ntiles; ++j) iter(j, std::false_type{});
+  // Tile 0 sets the references.  A wave with a column still without one (a
+  // mask hides its first keys) keeps taking tile maxima to the end; the
+  // others run the tiles without a maximum.
+  iter(0, std::false_type{}, std::false_type{});
+  int j = 1;
+  if (__builtin_amdgcn_ballot_w64(st.m == kNegInf) != 0)
+    for (; j <= ntiles; ++j) iter(j, std::false_type{}, std::false_type{});
+  for (; j < j_full; ++j) iter(j, std::true_type{}, std::true_type{});
+  for (; j <= ntiles; ++j) iter(j, std::false_type{}, std::true_type{});
 
   if (__any(over) && lane == 0) s_over = 1;
   __syncthreads();

@@ -180,3 +180,39 @@ def test_attend_logit_jump_past_the_reference(kind):
     torch.cuda.synchronize()
     ref = oracle_ref(inp["Q"], inp["K"], inp["V"], cfg.scale, mask)
     assert_parity(out, ref, torch.bfloat16, what)
+
+
+KEY_PAD_CASES = [
+    # dtype, m, dh, G: visible keys per sequence below
+    (torch.bfloat16, 300, 128, 1),
+    (torch.bfloat16, 300, 64, 2),
+    (torch.float32, 300, 128, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,m,dh,G", KEY_PAD_CASES)
+def test_attend_key_padding_edges(dtype, m, dh, G):
+    """A key-padding mask whose last visible key falls at and around tile
+    boundaries (32 keys), a sequence with every key hidden (zeros), keys
+    visible only in the middle, and only the very last key visible.  The
+    pipelined kernel stops each workgroup after the last tile with a visible
+    key; the hidden tiles must add exactly nothing."""
+    ends = [1, 31, 32, 33, 64, 65, 299, 300, 0]
+    b, n, h = len(ends) + 2, 9, 32
+    what = f"attend key padding edges {dtype} m={m} dh={dh} G={G}"
+    announce(what)
+    cfg = W.MemoryConfig("t", dtype, b, n, m, h, G, dh, m, m, 450 + dh + G)
+    inp = W.memory_inputs(cfg)
+    mask = torch.zeros(b, 1, 1, m)
+    for bi, e in enumerate(ends):
+        mask[bi, 0, 0, e:] = float("-inf")
+    mask[len(ends), 0, 0, :100] = float("-inf")      # visible [100, 150) only
+    mask[len(ends), 0, 0, 150:] = float("-inf")
+    mask[len(ends) + 1, 0, 0, :m - 1] = float("-inf")  # only the last key visible
+    out = mqa.attend(inp["Q"].cuda(), inp["K"].cuda(), inp["V"].cuda(), cfg.scale,
+                     mask=mask.cuda())
+    torch.cuda.synchronize()
+    ref = oracle_ref(inp["Q"], inp["K"], inp["V"], cfg.scale, mask)
+    assert_parity(out, ref, dtype, what)
+    # the sequence with every key hidden gives exact zeros
+    assert torch.count_nonzero(out[len(ends) - 1]).item() == 0
