@@ -60,8 +60,15 @@ __device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
 
-  const int rb = a.nrb - 1 - (int)(blockIdx.x % a.nrb);
-  const int bg = blockIdx.x / a.nrb;
+  // Causal: row blocks in order of decreasing length (the latest rows see
+  // the most keys) with the (sequence, group) pairs interleaved, so that no
+  // long block is left for the end and a pair's workgroups share an XCD's L2
+  // when the pair count divides the XCD count.  Otherwise pair-major: every
+  // XCD takes its share of every pair (pairs may differ in length when a
+  // key-padding mask cuts them short).
+  const int nbg = a.b * a.G;
+  const int rb = a.nrb - 1 - (int)(CAUSAL ? blockIdx.x / nbg : blockIdx.x % a.nrb);
+  const int bg = CAUSAL ? (int)(blockIdx.x % nbg) : (int)(blockIdx.x / a.nrb);
   const int bi = bg / a.G, g = bg % a.G;
   const int rows_per_block = NW * a.rpw;
   const int r_begin = rb * rows_per_block;
@@ -396,8 +403,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
 
-  const int rb = a.nrb - 1 - (int)(blockIdx.x % a.nrb);
-  const int bg = blockIdx.x / a.nrb;
+  // Causal: row blocks in order of decreasing length (the latest rows see
+  // the most keys) with the (sequence, group) pairs interleaved, so that no
+  // long block is left for the end and a pair's workgroups share an XCD's L2
+  // when the pair count divides the XCD count.  Otherwise pair-major: every
+  // XCD takes its share of every pair (pairs may differ in length when a
+  // key-padding mask cuts them short).
+  const int nbg = a.b * a.G;
+  const int rb = a.nrb - 1 - (int)(CAUSAL ? blockIdx.x / nbg : blockIdx.x % a.nrb);
+  const int bg = CAUSAL ? (int)(blockIdx.x % nbg) : (int)(blockIdx.x / a.nrb);
   const int bi = bg / a.G, g = bg % a.G;
   const int rows_per_block = NW * a.rpw;
   const int r_begin = rb * rows_per_block;
@@ -455,8 +469,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   auto issue = [&](int tile, Chunks& ld) {
     const int pos0 = tile * kTileRows + col;
     const int pos = pos0 < a.m ? pos0 : a.m - 1;
-    const char* kp = kseq + (size_t)pos * rs;
-    const char* vp = vseq + (size_t)pos * rs;
+    const uint64_t off = (uint64_t)(uint32_t)pos * (uint32_t)rs;  // one 32 x 32 -> 64 multiply
+    const char* kp = kseq + off;
+    const char* vp = vseq + off;
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int c = wave + i * NW;
