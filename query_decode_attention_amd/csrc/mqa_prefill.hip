@@ -15,10 +15,12 @@
 //
 // Workgroup.  NW waves cover NW*rpw consecutive rows of one (sequence, group)
 // and walk the key tiles [0, last row] once.  Per tile, the K rows and the V
-// rows (already transposed into the PV operand layout by an exact selection
-// MFMA) are staged in LDS once and read by all NW waves; LDS is double
-// buffered so the next tile's global loads overlap this tile's MFMAs.  Row
-// blocks are launched last-row-first so the longest causal rows start early.
+// rows are staged in LDS once and read by all NW waves, in several buffers so
+// that later tiles' global loads overlap this tile's MFMAs.  The fp32 kernel
+// stages V transposed into the PV operand layout (an exact selection MFMA);
+// the bf16 kernel stages V rows as they are and reads the operand with the
+// LDS transposing read.  Row blocks are launched last-row-first so the
+// longest causal rows start early.
 #include <type_traits>
 
 #include "mqa_device.h"
@@ -384,19 +386,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
   constexpr int NB = 4;                       // LDS tile buffers (a power of two)
-  constexpr int VPW = NQ / ND;                // V chunks per d block (2)
-  constexpr int KPW = (NQ + NW - 1) / NW;     // K chunks staged per wave
-  static_assert(NW >= ND, "a wave per d block transposes V");
-  static_assert(VPW == 2, "two V chunks per d block");
+  constexpr int CPW = 2 * NQ / NW;            // K and V chunks staged per wave and tile
+  static_assert(2 * NQ % NW == 0, "K and V chunks shared out evenly");
   constexpr bool BIAS = MASK != kMaskNone;
-  // Staging (a measured choice): causal prefill stages through registers one
-  // tile ahead; attention over a fixed memory loads straight into LDS.
-  constexpr bool DMA = !CAUSAL;
+  // K chunk c: entry `lane` holds the score product's operand fragment (key
+  // lane % 32, d 16c + 8 (lane / 32) ..).  V chunk c: entry 2 key + e holds
+  // d 16c + 8e .. of the key, so the chunk is the 32 keys' d range as 32-byte
+  // rows, which the PV operand reads transposed (read_vt below).
   __shared__ u32x4 s_k[NB][NQ][64];
-  __shared__ u32x4 s_vt[NB][ND][2][64];      // V transposed: the PV operand
-  __shared__ u32x4 s_vr[NB][NQ][64];         // V rows as loaded (direct staging)
-  __shared__ f32x4 s_kb[NB][kTileRows / 4];  // per-key mask of the tile (key padding)
-  __shared__ float s_kbw[NB][NW][64];        // the same, a copy per wave (direct staging)
+  __shared__ u32x4 s_v[NB][NQ][64];
+  __shared__ float s_kbw[NB][NW][64];  // per-key mask of the tile (key padding), a copy per wave
   __shared__ int s_over;                     // some column exceeded its reference
 
   const int lane = threadIdx.x & 63;
@@ -447,119 +446,52 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
     for (int c = 0; c < NQ; ++c) qr[c] = *reinterpret_cast<const u32x4*>(qp + (2 * c + half) * 16);
   }
 
-  SelOps<T> sel;
-  sel.init(col, half);
   const size_t rs = (size_t)a.G * DH * sizeof(T);
   const size_t seq_off = ((size_t)bi * a.m * a.G + (size_t)g) * DH * sizeof(T);
   const char* kseq = a.K + seq_off;
   const char* vseq = a.V + seq_off;
 
-  // Staging, one tile ahead: wave w loads K chunks w, w + NW, ...; waves
-  // below ND load and transpose d block `wave` of V; with a key-padding mask
-  // the last wave loads the tile's 32 values.  Positions past m read row
-  // m - 1 (finite; masked).
-  const bool v_wave = wave < ND;
-  const bool kb_wave = MASK == kMaskKeys && wave == NW - 1;
-  const float* kb_row = kb_wave ? a.mask + (int64_t)bi * a.msb : nullptr;
-  struct Chunks {
-    u32x4 k[KPW];
-    u32x4 v[VPW];
-    float kb;
-  };
-  auto issue = [&](int tile, Chunks& ld) {
-    const int pos0 = tile * kTileRows + col;
-    const int pos = pos0 < a.m ? pos0 : a.m - 1;
-    const uint64_t off = (uint64_t)(uint32_t)pos * (uint32_t)rs;  // one 32 x 32 -> 64 multiply
-    const char* kp = kseq + off;
-    const char* vp = vseq + off;
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int c = wave + i * NW;
-      if (c < NQ) ld.k[i] = *reinterpret_cast<const u32x4*>(kp + (2 * c + half) * 16);
-    }
-    if (v_wave) {
-#pragma unroll
-      for (int i = 0; i < VPW; ++i)
-        ld.v[i] = *reinterpret_cast<const u32x4*>(vp + (2 * (wave * VPW + i) + half) * 16);
-    }
-    if (kb_wave) ld.kb = kb_row[pos] * 1.4426950408889634f;  // log2 units
-  };
-  auto commit = [&](int buf, const Chunks& ld) {
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int c = wave + i * NW;
-      if (c < NQ) s_k[buf][c][lane] = ld.k[i];
-    }
-    if (v_wave) {
-      u32x4 ops[2];
-      transpose_block<T, VPW>(ld.v, 0, sel, ops);
-      s_vt[buf][wave][0][lane] = ops[0];
-      s_vt[buf][wave][1][lane] = ops[1];
-    }
-    if (kb_wave && half == 0) reinterpret_cast<float*>(s_kb[buf])[col] = ld.kb;
-  };
-
-  // Direct-to-LDS staging, three tiles ahead of the iteration that issues
-  // it: the 2*NQ chunks of K and V rows of a tile (1 KB each) are shared out
-  // evenly, wave w taking chunks w, w + NW, ...; with a key-padding mask
-  // every wave also fetches the tile's mask values into a slot of its own.
-  // In iteration t, before its barrier, the waves below ND transpose d
-  // block `wave` of the V rows of tile t + 1 into the PV operand layout.
-  constexpr int CPW = 2 * NQ / NW;  // chunks per wave and tile
-  static_assert(!DMA || 2 * NQ % NW == 0, "K and V chunks shared out evenly");
-  const float* kbw_row = MASK == kMaskKeys ? a.mask + (int64_t)bi * a.msb : nullptr;
+  // Staging, straight into LDS (global_load_lds) three tiles ahead: the
+  // 2*NQ chunks of a tile's K and V rows (1 KB each) are shared out evenly,
+  // wave w taking chunks w, w + NW, ... (K chunks first).  A K chunk is
+  // loaded in its operand layout (lane: key lane % 32, d half lane / 32), a
+  // V chunk as 32-byte rows (lane: key lane / 2, d half lane % 2), so both
+  // land lane by lane, contiguously.  Positions past m read row m - 1
+  // (finite; masked).  With a key-padding mask every wave also fetches the
+  // tile's mask values into a slot of its own.  Tile t + 3 is issued after
+  // iteration t's barrier, by which every wave is done with the buffer it
+  // refills (that of tile t - 1, whose last reader is PV(t - 1) before the
+  // barrier).
   const uint32_t rs32 = (uint32_t)rs;
+  // byte offsets of this lane's K and V rows of a tile (positions clamped;
+  // one 32 x 32 -> 64-bit multiply each)
+  auto row_offsets = [&](int tile, uint32_t& pos_k, uint64_t& off_k, uint64_t& off_v) {
+    const int pk = tile * kTileRows + col, pv_ = tile * kTileRows + (lane >> 1);
+    pos_k = (uint32_t)(pk < a.m ? pk : a.m - 1);
+    off_k = (uint64_t)pos_k * rs32;
+    off_v = (uint64_t)(uint32_t)(pv_ < a.m ? pv_ : a.m - 1) * rs32;
+  };
+  const float* kbw_row = MASK == kMaskKeys ? a.mask + (int64_t)bi * a.msb : nullptr;
+  constexpr int kPerTile = CPW + (MASK == kMaskKeys ? 1 : 0);  // loads per wave and tile
+  static_assert(2 * kPerTile <= 15, "vmcnt immediate");
   auto issue_dma = [&](int tile) {
-    const int pos0 = tile * kTileRows + col;
-    const uint32_t pos = (uint32_t)(pos0 < a.m ? pos0 : a.m - 1);
-    const uint64_t off = (uint64_t)pos * rs32;  // one 32 x 32 -> 64-bit multiply
+    uint32_t pos;
+    uint64_t off_k, off_v;
+    row_offsets(tile, pos, off_k, off_v);
     const int buf = tile & (NB - 1);
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = wave + i * NW;  // wave-uniform
       if (c < NQ)
-        load_to_lds(kseq + off + (2 * c + half) * 16, &s_k[buf][c][0]);
+        load_to_lds(kseq + off_k + (2 * c + half) * 16, &s_k[buf][c][0]);
       else
-        load_to_lds(vseq + off + (2 * (c - NQ) + half) * 16, &s_vr[buf][c - NQ][0]);
+        load_to_lds(vseq + off_v + (2 * (c - NQ) + (lane & 1)) * 16, &s_v[buf][c - NQ][0]);
     }
     // lanes 32..63 repeat lanes 0..31 into the slot's second half
     if constexpr (MASK == kMaskKeys)
       __builtin_amdgcn_global_load_lds((const void*)(kbw_row + pos),
                                        (__attribute__((address_space(3))) void*)&s_kbw[buf][wave][0],
                                        4, 0, 0);
-  };
-  auto transpose_v = [&](int t) {
-    const int buf = t & (NB - 1);
-    // The compiler cannot tell these reads from the locations that
-    // direct-to-LDS loads still in flight write, and would wait for all of
-    // them; the rows were published by the issuing waves' waits and a
-    // barrier, so the reads are issued here with a wait of their own.
-    u32x4 vr[VPW];
-    const uint32_t addr = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) u32x4*)&s_vr[buf][wave * VPW][lane]);
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %2 offset:1024\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(vr[0]), "=&v"(vr[1])
-        : "v"(addr)
-        : "memory");
-    u32x4 ops[2];
-    transpose_block<T, VPW>(vr, 0, sel, ops);
-    s_vt[buf][wave][0][lane] = ops[0];
-    s_vt[buf][wave][1][lane] = ops[1];
-  };
-  // Loads each wave issues per tile.  Tile t has landed once at most the
-  // loads issued after it are outstanding (loads complete in order): those
-  // of tile t + 1, if there is one.
-  constexpr int kPerTile = CPW + (MASK == kMaskKeys ? 1 : 0);
-  static_assert(kPerTile <= 15, "vmcnt immediate");
-  auto wait_tile = [&](int t) {
-    if (t >= ntiles) return;
-    if (t + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
   // additive mask row of this lane's column (general mask only)
@@ -575,49 +507,75 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   p_prev[0] = p_prev[1] = bf16x8{};
   bool over = false;
 
-  auto scores = [&](int buf, const f32x16& init) {
-    u32x4 kr[NQ];
+  auto read_k = [&](int buf, u32x4 (&kr)[NQ]) {
 #pragma unroll
     for (int c = 0; c < NQ; ++c) kr[c] = s_k[buf][c][lane];
+  };
+  auto scores_of = [&](const u32x4 (&kr)[NQ], const f32x16& init) {
     f32x16 s = init;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) s = mfma_bf16(as_bf16x8(kr[c]), as_bf16x8(qr[c]), s);
     return s;
   };
-  auto pv = [&](int buf) {
-    u32x4 vr[ND][2];
+  // The PV operand V^T (row d, 8 keys per lane) of d block db and keys
+  // 16k .. 16k + 15, read transposed from the V rows in LDS: within each
+  // group of 16 lanes, a transposing read hands lane 4u + e element e of the
+  // 8-byte rows addressed by lanes u, u + 4, u + 8, u + 12.  Lane l addresses
+  // key 4 (l / 32) + (l % 16) / 4 (+ 8 for the second read), d 16 ((l / 16)
+  // % 2) + 4 (l % 4) of the block, so it receives d = l % 32 and keys
+  // 4 (l / 32) + 0..3 and 8 + 4 (l / 32) + 0..3: the key order of the
+  // probability operand (registers d_row(r, l / 32)).
+  const int vt_lane = ((lane >> 4) & 1) * 1024 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 32 +
+                      8 * (lane & 3);
+  auto read_vt = [&](int buf, int db, int k) {
+    using lds_bf16x4 = __attribute__((address_space(3))) bf16x4;
+    auto base = (__attribute__((address_space(3))) char*)&s_v[buf][0][0] + vt_lane + db * 2048 + k * 512;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 256));
+    return bf16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto read_v = [&](int buf, bf16x8 (&vt)[ND][2]) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) vr[d][k] = s_vt[buf][d][k][lane];
+      for (int k = 0; k < 2; ++k) vt[d][k] = read_vt(buf, d, k);
+  };
+  auto pv_of = [&](const bf16x8 (&vt)[ND][2]) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      st.o[d] = mfma_bf16(as_bf16x8(vr[d][0]), p_prev[0], st.o[d]);
-      st.o[d] = mfma_bf16(as_bf16x8(vr[d][1]), p_prev[1], st.o[d]);
+      st.o[d] = mfma_bf16(vt[d][0], p_prev[0], st.o[d]);
+      st.o[d] = mfma_bf16(vt[d][1], p_prev[1], st.o[d]);
     }
   };
   // Mask values of tile j, register r holding key d_row(r, half), in log2
-  // units (masked kinds only).
-  auto load_bias = [&](int j, float (&bias)[16]) {
+  // units times `post` (masked kinds only).
+  auto load_bias = [&](int j, float (&bias)[16], float post) {
     if constexpr (MASK == kMaskKeys) {
       // keys 8k + 4*half .. +3 of the tile for registers 4k .. 4k+3
+      // (read with a wait of its own: behind the next tile's direct-to-LDS
+      // loads, the compiler would make the reads wait for those loads)
+      f32x4 kb[4];
+      const uint32_t addr = (uint32_t)(uintptr_t)(
+          (__attribute__((address_space(3))) char*)&s_kbw[j & (NB - 1)][wave][0] + 16 * half);
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:32\n\t"
+          "ds_read_b128 %2, %4 offset:64\n\t"
+          "ds_read_b128 %3, %4 offset:96\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kb[0]), "=&v"(kb[1]), "=&v"(kb[2]), "=&v"(kb[3])
+          : "v"(addr)
+          : "memory");
+      const float mult = kLog2e * post;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (DMA) {
-          const f32x4 kb = reinterpret_cast<const f32x4*>(s_kbw[j & (NB - 1)][wave])[2 * k + half];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e] * kLog2e;
-        } else {
-          const f32x4 kb = s_kb[j & (NB - 1)][2 * k + half];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[e];
-        }
-      }
+        for (int e = 0; e < 4; ++e) bias[4 * k + e] = kb[k][e] * mult;
     } else if constexpr (MASK == kMaskFull) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int jj = j * kTileRows + d_row(r, half);
-        bias[r] = (mrow && jj < a.m) ? mrow[jj] * kLog2e : 0.f;
+        bias[r] = (mrow && jj < a.m) ? mrow[jj] * (kLog2e * post) : 0.f;
       }
     }
   };
@@ -630,9 +588,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
     f32x16 init = {};
     if constexpr (FOLD && BIAS) {
       float b[16];
-      load_bias(j, b);
+      load_bias(j, b, inv_c);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) init[r] = b[r] * inv_c;
+      for (int r = 0; r < 16; ++r) init[r] = b[r];
     }
     return init;
   };
@@ -644,62 +602,75 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   // hidden, which leaves (m, l, O) unchanged and yields P = 0, so the next PV
   // adds exactly zero; the score product of a tile no one will read is
   // discarded the same way.
-  Chunks ld;
+  //
+  // The iteration runs in two halves around the barrier that publishes tile
+  // j + 1.  Before it: PV of tile j - 1 (tile 0's buffer when j = 0: finite,
+  // and P = 0) and the softmax of tile j, whose operands earlier barriers
+  // published, so a wave waiting at the barrier has its products in flight
+  // and the waves' LDS reads spread out.  After it: the scores of tile j + 1.
+  // Tile j + 3's loads are issued after the iteration's last LDS operand
+  // read (the compiler would make any LDS read behind them wait for them).
   auto iter = [&](int j, auto full_tile, auto ref_known) {
     constexpr bool FULL = decltype(full_tile)::value;
     constexpr bool REF = decltype(ref_known)::value;
-    if constexpr (DMA) {
-      if (j + 3 < ntiles) issue_dma(j + 3);
-      if (v_wave && j + 1 < ntiles) transpose_v(j + 1);
-      wait_tile(j + 2);
-      lds_barrier();
-    } else {
-      if (j + 1 < ntiles) {
-        commit((j + 1) & (NB - 1), ld);
-        if (j + 2 < ntiles) issue(j + 2, ld);
-      }
-      __syncthreads();
-    }
-    // PV of tile j - 1 (tile 0's buffer when j = 0: finite, and P = 0)
-    pv(j == 0 ? 0 : (j - 1) & (NB - 1));
+    // this wave's part of tile j + 1 (issued in iteration j - 2) landed;
+    // tile j + 2 may stay in flight
+    if (j + 2 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
+    else if (j + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    bf16x8 vt[ND][2];
+    read_v(j == 0 ? 0 : (j - 1) & (NB - 1), vt);
     float bias[16];
-    if constexpr (SM_BIAS) load_bias(j, bias);
+    if constexpr (SM_BIAS) load_bias(j, bias, 1.0f);
+    pv_of(vt);
     bf16x8 p_cur[2];
     softmax_fixed<ND, FULL, SM_BIAS, FOLD, REF>(st, s_cur, a.scale_log2, j * kTileRows,
                                            j < w_tiles ? lim : -1, half, p_cur, bias, over);
-    s_cur = scores((j + 1) & (NB - 1), score_init(j + 1));
     p_prev[0] = p_cur[0];
     p_prev[1] = p_cur[1];
     if constexpr (FULL) {
       // the LDS operands first, then the MFMAs spread over the vector work
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * ND + NQ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * ND + NQ; ++i) {
+      for (int i = 0; i < 2 * ND; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
       }
+    }
+    lds_barrier();
+    u32x4 kr[NQ];
+    read_k((j + 1) & (NB - 1), kr);
+    // a general mask comes from global memory: loaded before the next tile's
+    // loads, since loads complete in order
+    f32x16 init;
+    if constexpr (MASK == kMaskFull) init = score_init(j + 1);
+    if (j + 3 < ntiles) issue_dma(j + 3);
+    if constexpr (MASK != kMaskFull) init = score_init(j + 1);
+    s_cur = scores_of(kr, init);
+    if constexpr (FULL) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NQ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
     }
   };
 
-  // prologue: tile 0 staged and its scores computed, tile 1 loaded
-  if constexpr (DMA) {
-    // tiles 0, 1 and 2 in flight; 0 and 1 landed and published, 0 transposed
-    issue_dma(0);
-    if (ntiles > 1) issue_dma(1);
-    if (ntiles > 2) issue_dma(2);
-    if (ntiles > 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    lds_barrier();
-    if (v_wave) transpose_v(0);
-  } else {
-    issue(0, ld);
-    commit(0, ld);
-    if (ntiles > 1) issue(1, ld);
-    __syncthreads();
+  // prologue: tiles 0, 1 and 2 in flight, 0 landed and published, its
+  // scores computed
+  issue_dma(0);
+  if (ntiles > 1) issue_dma(1);
+  if (ntiles > 2) issue_dma(2);
+  if (ntiles > 2)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kPerTile));
+  else if (ntiles > 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
+  {
+    u32x4 kr[NQ];
+    read_k(0, kr);
+    s_cur = scores_of(kr, score_init(0));
   }
-  s_cur = scores(0, score_init(0));
   // Tile 0 sets the references.  A wave with a column still without one (a
   // mask hides its first keys) keeps taking tile maxima to the end; the
   // others run the tiles without a maximum.
