@@ -394,7 +394,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   // d 16c + 8e .. of the key, so the chunk is the 32 keys' d range as 32-byte
   // rows, which the PV operand reads transposed (read_vt below).
   __shared__ u32x4 s_k[NB][NQ][64];
-  __shared__ u32x4 s_v[NB][NQ][64];
+  // (V chunks 1152 bytes apart: the two chunks of a 32-wide d block, read
+  // by lanes 0-15 and 16-31 of one transposing read, then fall in different
+  // LDS banks)
+  __shared__ u32x4 s_v[NB][NQ][72];
   __shared__ float s_kbw[NB][NW][64];  // per-key mask of the tile (key padding), a copy per wave
   __shared__ int s_over;                     // some column exceeded its reference
 
@@ -525,11 +528,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   // % 2) + 4 (l % 4) of the block, so it receives d = l % 32 and keys
   // 4 (l / 32) + 0..3 and 8 + 4 (l / 32) + 0..3: the key order of the
   // probability operand (registers d_row(r, l / 32)).
-  const int vt_lane = ((lane >> 4) & 1) * 1024 + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 32 +
+  constexpr int kVChunk = sizeof(s_v[0][0]);  // bytes between V chunks
+  const int vt_lane = ((lane >> 4) & 1) * kVChunk + (4 * (lane >> 5) + ((lane & 15) >> 2)) * 32 +
                       8 * (lane & 3);
   auto read_vt = [&](int buf, int db, int k) {
     using lds_bf16x4 = __attribute__((address_space(3))) bf16x4;
-    auto base = (__attribute__((address_space(3))) char*)&s_v[buf][0][0] + vt_lane + db * 2048 + k * 512;
+    auto base = (__attribute__((address_space(3))) char*)&s_v[buf][0][0] + vt_lane +
+                db * 2 * kVChunk + k * 512;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 256));
     return bf16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
