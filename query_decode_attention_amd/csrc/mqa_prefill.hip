@@ -608,13 +608,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   // adds exactly zero; the score product of a tile no one will read is
   // discarded the same way.
   //
-  // The iteration runs in two halves around the barrier that publishes tile
-  // j + 1.  Before it: PV of tile j - 1 (tile 0's buffer when j = 0: finite,
-  // and P = 0) and the softmax of tile j, whose operands earlier barriers
-  // published, so a wave waiting at the barrier has its products in flight
-  // and the waves' LDS reads spread out.  After it: the scores of tile j + 1.
-  // Tile j + 3's loads are issued after the iteration's last LDS operand
-  // read (the compiler would make any LDS read behind them wait for them).
+  // The iteration's barrier publishes tile j + 1.  The V^T operand of PV of
+  // tile j - 1 (tile 0's buffer when j = 0: finite, and P = 0), published by
+  // an earlier barrier, is read before it, the K operand of the scores of
+  // tile j + 1 after it; the products and the softmax go where the compiler
+  // schedules them (keeping PV and the softmax ahead of the barrier measured
+  // slower).  Tile j + 3's loads are issued after the iteration's last LDS
+  // operand read (the compiler would make any LDS read behind them wait for
+  // them).
   auto iter = [&](int j, auto full_tile, auto ref_known) {
     constexpr bool FULL = decltype(full_tile)::value;
     constexpr bool REF = decltype(ref_known)::value;
