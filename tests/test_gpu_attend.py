@@ -52,6 +52,8 @@ GRID = [
     (torch.bfloat16, 1, 40, 500, 32, 8, 128, "pad"),
     (torch.bfloat16, 2, 1, 300, 32, 1, 128, "full_inf"),
     (torch.float32, 1, 20, 45, 8, 1, 64, "pad"),
+    (torch.bfloat16, 2, 20, 90, 8, 1, 64, "full"),      # d_h 64: V^T read transposed, padded chunks
+    (torch.bfloat16, 1, 33, 165, 16, 4, 64, "pad"),
 ]
 
 

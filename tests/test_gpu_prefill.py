@@ -24,6 +24,7 @@ CASES = [
     (torch.bfloat16, 1, 257, 32, 4, 128),   # GQA h/G = 8 (4 rows per wave)
     (torch.bfloat16, 2, 70, 4, 4, 64),      # MHA h/G = 1 (32 rows per wave)
     (torch.bfloat16, 1, 64, 12, 1, 64),     # h/G = 12 padded to 16
+    (torch.bfloat16, 1, 300, 32, 1, 64),    # d_h 64, ten key tiles in flight three ahead
     (torch.float32, 1, 90, 8, 2, 128),
     (torch.float32, 2, 33, 32, 1, 64),
 ]
