@@ -48,16 +48,31 @@ constexpr int kMaskNone = 0, kMaskKeys = 1, kMaskFull = 2;
 // (Not inlined: the bf16 kernel calls it only to recompute a workgroup whose
 // logits outgrew their fixed softmax reference, and inlining it there would
 // add its registers to the bf16 kernel's hot loops.)
+//
+// Its LDS comes from the caller: the fp32 kernel's own arrays, or, in the
+// bf16 kernel's rescue, the bf16 loops' tile buffers (free by then).
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+template <typename T, int DH>
+struct RowsLds {
+  using S = TileShape<T, DH>;
+  static constexpr size_t kBytesK = 2 * S::NQ * 64 * sizeof(u32x4);               // s_k[2][NQ][64]
+  static constexpr size_t kBytesVt = 2 * S::ND * S::VTC * 64 * sizeof(u32x4);    // s_vt[2][ND][VTC][64]
+  static constexpr size_t kBytesKb = 2 * (kTileRows / 4) * sizeof(f32x4);        // s_kb[2][8]
+};
 template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
-__device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a) {
+__device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a, lds_u32x4* k_mem,
+                                                       lds_u32x4* vt_mem, lds_f32x4* kb_mem) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND, VTC = S::VTC;
   static_assert(NW >= ND, "a wave per d block transposes V");
   constexpr int KPW = (NQ + NW - 1) / NW;     // K chunks per wave
   constexpr int VPW = NQ / ND;                // V chunks per d block
-  __shared__ u32x4 s_k[2][NQ][64];
-  __shared__ u32x4 s_vt[2][ND][VTC][64];
-  __shared__ f32x4 s_kb[2][kTileRows / 4];  // per-key mask of the tile (key padding)
+  lds_u32x4 (*const s_k)[NQ][64] = reinterpret_cast<lds_u32x4 (*)[NQ][64]>(k_mem);
+  lds_u32x4 (*const s_vt)[ND][VTC][64] = reinterpret_cast<lds_u32x4 (*)[ND][VTC][64]>(vt_mem);
+  // per-key mask of the tile (key padding)
+  lds_f32x4 (*const s_kb)[kTileRows / 4] = reinterpret_cast<lds_f32x4 (*)[kTileRows / 4]>(kb_mem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -147,7 +162,7 @@ __device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a) {
 #pragma unroll
       for (int k = 0; k < VTC; ++k) s_vt[buf][wave][k][lane] = ops[k];
     }
-    if (kb_wave && half == 0) reinterpret_cast<float*>(s_kb[buf])[col] = ld.kb;
+    if (kb_wave && half == 0) reinterpret_cast<lds_float*>(s_kb[buf])[col] = ld.kb;
   };
 
   // additive mask row of this lane's column (non-causal only)
@@ -246,7 +261,11 @@ __device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a) {
 
 template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
-  prefill_rows<T, DH, NW, CAUSAL, FOLD, MASK>(a);
+  using L = RowsLds<T, DH>;
+  __shared__ u32x4 s_k[L::kBytesK / sizeof(u32x4)];
+  __shared__ u32x4 s_vt[L::kBytesVt / sizeof(u32x4)];
+  __shared__ f32x4 s_kb[L::kBytesKb / sizeof(f32x4)];
+  prefill_rows<T, DH, NW, CAUSAL, FOLD, MASK>(a, (lds_u32x4*)s_k, (lds_u32x4*)s_vt, (lds_f32x4*)s_kb);
 }
 
 // ------------------------------------------------------------ bf16 kernel
@@ -258,12 +277,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 //     softmax(j): S_j -> P_j                      (VALU: max, exp2, bf16 pack)
 //     S(j+1) = K_{j+1} . Q^T                      (MFMA)
 // and neither product depends on the softmax between them, so the scheduler
-// is asked to interleave them.  Four LDS buffers: iteration j stages tile
-// j+1 into the buffer of tile j-3, whose last reader (PV of j-3) ran in
-// iteration j-2, so the barrier of iteration j-1 separates every read of a
-// buffer from its next write.  Tiles that every wave of the workgroup sees in
-// full run in a loop without any masking; the diagonal and the tiles after
-// it run in a second loop whose softmax masks by position.
+// is asked to interleave them.  K and V rows go straight into four LDS tile
+// buffers, three tiles ahead (see the staging below), and the PV operand is
+// read transposed from the V rows.  Tiles that every wave of the workgroup
+// sees in full run in a loop without any masking; the diagonal and the tiles
+// after it run in a second loop whose softmax masks by position.
 //
 // The softmax packs its probabilities two at a time (v_cvt_pk_bf16_f32) and
 // sums the packed, rounded values with v_dot2_f32_bf16 against (1, 1), so the
@@ -380,8 +398,10 @@ __device__ __forceinline__ void softmax_fixed(WaveState<ND>& st, const f32x16& s
   }
 }
 
+// (at least two waves per SIMD: with four-wave workgroups, two share a CU)
 template <int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(
+    PrefillArgs a) {
   using T = __bf16;
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
@@ -692,7 +712,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   if (s_over) {
     // some logit exceeded its column's fixed reference by more than the
     // slack: recompute the workgroup's rows with the rescaling kernel body
-    prefill_rows<T, DH, NW, CAUSAL, false, MASK>(a);
+    // (its LDS: the K tile buffers for its K and V^T tiles, a V tile buffer
+    // for its mask values; every wave is past the loops)
+    using RL = RowsLds<T, DH>;
+    static_assert(RL::kBytesK + RL::kBytesVt <= sizeof(s_k) && RL::kBytesKb <= sizeof(s_v),
+                  "the rescue fits the tile buffers");
+    lds_u32x4* const kmem = (lds_u32x4*)&s_k[0][0][0];
+    prefill_rows<T, DH, NW, CAUSAL, false, MASK>(a, kmem, kmem + RL::kBytesK / sizeof(u32x4),
+                                                 (lds_f32x4*)&s_v[0][0][0]);
     return;
   }
 
@@ -730,10 +757,13 @@ __global__ void prefill_cache_copy_kernel(const char* K, const char* V, char* ck
 }
 
 namespace {
-constexpr int kPrefillWaves = 8;
+constexpr int kPrefillWaves = 8;      // fp32 workgroups
+constexpr int kPrefillWavesBf16 = 8;  // bf16 workgroups
+template <typename T>
+constexpr int prefill_waves() { return sizeof(T) == 2 ? kPrefillWavesBf16 : kPrefillWaves; }
 
 // Row blocks of NW * rpw query rows per (sequence, group).
-PrefillArgs row_blocks(const PrefillParams& p, int m) {
+PrefillArgs row_blocks(const PrefillParams& p, int m, int nw) {
   PrefillArgs a;
   a.Q = (const char*)p.Q;
   a.K = (const char*)p.K;
@@ -751,7 +781,7 @@ PrefillArgs row_blocks(const PrefillParams& p, int m) {
   while (hgp < a.hg) hgp *= 2;
   a.hgp = hgp;
   a.rpw = 32 / hgp;
-  const int rows_per_block = kPrefillWaves * a.rpw;
+  const int rows_per_block = nw * a.rpw;
   a.nrb = (p.n + rows_per_block - 1) / rows_per_block;
   a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
   return a;
@@ -761,12 +791,13 @@ PrefillArgs row_blocks(const PrefillParams& p, int m) {
 // (fp32 operands twice as wide) otherwise.
 template <typename T, int DH, bool CAUSAL, bool FOLD, int MASK>
 void launch_rows(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int NW = prefill_waves<T>();
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((prefill_bf16_kernel<DH, kPrefillWaves, CAUSAL, FOLD, MASK>), grid,
-                       dim3(kPrefillWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<DH, NW, CAUSAL, FOLD, MASK>), grid, dim3(NW * 64), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, DH, kPrefillWaves, CAUSAL, FOLD, MASK>), grid,
-                       dim3(kPrefillWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<T, DH, NW, CAUSAL, FOLD, MASK>), grid, dim3(NW * 64), 0, s,
+                       a);
 }
 
 template <typename T, int DH>
@@ -784,7 +815,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const PrefillArgs a = row_blocks(p, p.n);
+  const PrefillArgs a = row_blocks(p, p.n, prefill_waves<T>());
   const dim3 grid((unsigned)((size_t)p.b * p.G * a.nrb));
   if (a.scale_log2 > 0.f)
     launch_rows<T, DH, true, true, kMaskNone>(a, grid, s);
@@ -795,7 +826,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
 
 template <typename T, int DH>
 hipError_t launch_attend_t(const AttendParams& q, hipStream_t s) {
-  PrefillArgs a = row_blocks(q.base, q.m);
+  PrefillArgs a = row_blocks(q.base, q.m, prefill_waves<T>());
   a.mask = q.mask;
   a.msb = q.msb;
   a.msh = q.msh;
