@@ -360,7 +360,9 @@ __device__ __forceinline__ void copy_q_own(const DecodeArgs& a, u32x4 (*dst)[64]
 
 // ------------------------------------------------------------ decode: kernel ----
 
-template <typename T, int DH, int NW>
+// WHOLE: every segment goes whole to the workgroup whose unit range holds its
+// first unit (no partial records; see launch_decode_t).
+template <typename T, int DH, int NW, bool WHOLE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using S = TileShape<T, DH>;
   constexpr int NQ = S::NQ, ND = S::ND;
@@ -632,11 +634,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const int unit = nb + lead;  // units of one group of this sequence
       const int g = a.G == 1 ? 0 : (t - seg_base) / unit;  // MQA: no division
       const int seg0 = seg_base + g * unit + lead;  // its first tile
-      const int ta = (t > seg0 ? t : seg0) - seg0;
-      const int te = (t1 < seg0 + nb ? t1 : seg0 + nb) - seg0;
-      if (te <= ta) {  // the range ends inside this segment's lead-in units
-        t = t1;
-        break;
+      int ta, te;
+      if constexpr (WHOLE) {
+        // whole segments: those whose first unit lies in [t0, t1)
+        if (seg0 - lead >= t1) {  // the next workgroup's
+          t = t1;
+          break;
+        }
+        ta = 0;
+        te = nb;
+        if (seg0 - lead < t0) {  // the previous workgroup's
+          t = seg0 + nb;
+          if (g == a.G - 1) {
+            seg_base += a.G * unit;
+            ++b_cur;
+          }
+          continue;
+        }
+      } else {
+        ta = (t > seg0 ? t : seg0) - seg0;
+        te = (t1 < seg0 + nb ? t1 : seg0 + nb) - seg0;
+        if (te <= ta) {  // the range ends inside this segment's lead-in units
+          t = t1;
+          break;
+        }
       }
       if (lane == np) {
         p_b = b_cur;
@@ -1108,12 +1129,15 @@ constexpr int kDecodeWaves = 8;
 // heads of one segment.  Small blocks spread the records of a small step over
 // many CUs (a CU streams only ~20 GB/s).
 constexpr int kCombineThreads = 128;
+// Cache capacity (tiles) up to which a decode without an append takes every
+// segment whole (see launch_decode_t).
+constexpr int kWholeMaxTiles = 8;
 
 // Workgroups of the decode launch for these shapes on the current device:
 // CUs x occupancy, cut to the largest grid the shapes can use.
 template <typename T, int DH>
 hipError_t decode_grid_t(const DecodeParams& p, int* grid_out) {
-  auto kern = decode_kernel<T, DH, kDecodeWaves>;
+  auto kern = decode_kernel<T, DH, kDecodeWaves, false>;
   int dev = 0;
   const int cus = current_device_cus(&dev);
   if (cus <= 0) return hipErrorInvalidDevice;
@@ -1150,7 +1174,6 @@ hipError_t decode_grid(const DecodeParams& p, int* grid) {
 
 template <typename T, int DH>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  auto kern = decode_kernel<T, DH, kDecodeWaves>;
   int grid = 0;
   if (hipError_t e = decode_grid_t<T, DH>(p, &grid); e != hipSuccess) return e;
 
@@ -1173,12 +1196,25 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   a.window = p.window;
   a.rec_floats = (int)(decode_record_bytes(a.hg, DH) / sizeof(float));
   a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  // Short caches without an append: every segment goes whole to one
+  // workgroup (the one whose unit range holds its first unit; the ranges
+  // stay balanced to within one short segment), so no partial record is
+  // written and the combine is not launched.  (An append needs the combine
+  // for the lens bump, which must follow every workgroup's read of lens.)
+  const bool whole =
+      p.k_new == nullptr && (p.m_cap + kTileRows - 1) / kTileRows <= kWholeMaxTiles;
   hipError_t e;
   if (p.ev_begin && (e = hipEventRecord(p.ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kDecodeWaves * 64), 0, s, a);
+  if (whole)
+    hipLaunchKernelGGL((decode_kernel<T, DH, kDecodeWaves, true>), dim3(grid),
+                       dim3(kDecodeWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, DH, kDecodeWaves, false>), dim3(grid),
+                       dim3(kDecodeWaves * 64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_end && (e = hipEventRecord(p.ev_end, s)) != hipSuccess) return e;
+  if (whole) return hipSuccess;
 
   CombineArgs ca;
   ca.prefix = a.prefix;

@@ -79,6 +79,42 @@ def test_decode_parity_grid(case):
     assert_parity(o, ref, dtype, f"grid {case}")
 
 
+# Caches of at most 8 tiles, decoded without an append: every segment goes
+# whole to one workgroup, so the library writes no partial records (and does
+# not launch the combine).  The workspace is filled with a sentinel first; past
+# its schedule header ((b + 4) int32, padded to 256 bytes) it must still hold
+# it afterwards.
+WHOLE_CASES = [
+    # dtype, b, h, G, dh, m_cap, lens range
+    (torch.bfloat16, 300, 32, 1, 128, 256, 0, 256),     # MQA, ragged, empty sequences
+    (torch.bfloat16, 1024, 8, 1, 128, 128, 128, 128),   # the pages' setting (uniform lengths)
+    (torch.bfloat16, 77, 16, 4, 64, 200, 1, 200),       # GQA, d_h 64
+    (torch.bfloat16, 2, 32, 32, 128, 64, 1, 64),        # MHA, fewer segments than workgroups
+    (torch.float32, 50, 8, 2, 128, 96, 0, 96),
+]
+
+
+@pytest.mark.parametrize("case", WHOLE_CASES, ids=lambda c: f"{str(c[0])[6:]}-b{c[1]}h{c[2]}G{c[3]}d{c[4]}m{c[5]}")
+def test_decode_short_caches_whole_segments(case):
+    dtype, b, h, G, dh, m_cap, lo, hi = case
+    announce(f"decode whole segments {case}")
+    cfg, inp = make(dtype, b, h, G, dh, m_cap, lo, hi, seed=7400 + b + h + G + dh)
+    d = to_dev(inp)
+    ws = mqa.workspace_for(h, d["K"])
+    ws.fill_(0xAB)
+    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle_step(inp, cfg.scale)
+    assert_parity(o, ref, dtype, f"whole {case}")
+    header = ((b + 4) * 4 + 255) // 256 * 256
+    assert bool((ws[header:] == 0xAB).all()), "a partial record was written"
+    # a window over the same caches (still whole segments)
+    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, window=17, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle_step(inp, cfg.scale, window=17)
+    assert_parity(o, ref, dtype, f"whole window {case}")
+
+
 @pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
 def test_decode_many_sequences_multi_chunk_scan(append, fused):
     """b > 64 exercises the multi-chunk wave scan of the schedule."""
