@@ -120,7 +120,9 @@ size_t mqa_decode_workspace_size(int32_t h, const mqa_cache* cache);
 /* mqa_decode -- one decode step (study notes section 4:
  * o_i = softmax(q_i K^T * scale) V; paper review section 3 einsums
  * "bhk,bmk->bhm", softmax, "bhm,bmv->bhv").  Two kernel launches: the
- * split-K attention, then the exact merge of segments it split.
+ * split-K attention, then the exact merge of segments it split; one launch
+ * when the cache holds at most 8 tiles of 32 positions (m_cap <= 256),
+ * where every sequence is kept whole in one workgroup.
  *   q      : device [b][h][d_h].
  *   lens   : device int32 [b] (read only); sequence b attends over positions
  *            [max(0, L - window), L) with L = clamp(lens[b], 0, m_cap).
