@@ -360,8 +360,9 @@ __device__ __forceinline__ void copy_q_own(const DecodeArgs& a, u32x4 (*dst)[64]
 
 // ------------------------------------------------------------ decode: kernel ----
 
-// WHOLE: every segment goes whole to the workgroup whose unit range holds its
-// first unit (no partial records; see launch_decode_t).
+// WHOLE: workgroup w takes sequences [b w / W, b (w + 1) / W), every group of
+// each, whole: no partial records, and the lens bump after an append done
+// here (see launch_decode_t).
 template <typename T, int DH, int NW, bool WHOLE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using S = TileShape<T, DH>;
@@ -428,6 +429,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // before chunk `lane` (chunk layout, up to 64 chunks), so that the range
   // search needs one block or chunk only.
   int ch_t = 0, ch_ne = 0;
+  // (WHOLE: no pass over lens; each workgroup reads its own sequences' only)
+  if constexpr (!WHOLE) {
   if (nchunks == 1) {  // b <= 64: one chunk, a compact path
     raw0 = lane < a.b ? a.lens[lane] : 0;
     sel.init(row, half);
@@ -475,6 +478,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   }
   }
+  }
   tiles = __builtin_amdgcn_readfirstlane(tiles);
   nonempty = __builtin_amdgcn_readfirstlane(nonempty);
   const bool small = (int64_t)tiles * a.G <= (int64_t)NW * gridDim.x;
@@ -486,8 +490,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int segs = nonempty * a.G;
   // Workgroups in use (see effective_grid): every wave has work, short
   // segments still run side by side.
-  const int W = effective_grid<NW>(Tt, segs, gridDim.x, small);
-  const int t0 = wg_start(Tt, blockIdx.x, W), t1 = wg_start(Tt, blockIdx.x + 1, W);
+  const int W = WHOLE ? 1 : effective_grid<NW>(Tt, segs, gridDim.x, small);
+  const int t0 = WHOLE ? 0 : wg_start(Tt, blockIdx.x, W);
+  const int t1 = WHOLE ? 0 : wg_start(Tt, blockIdx.x + 1, W);
   // Units of the sequences of one chunk: their tiles plus `lead` per non-empty
   // sequence; u_excl / u_incl are prefixes within the chunk.
   auto chunk_units = [&](int v, int incl, int& u, int& u_incl) {
@@ -501,6 +506,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   int cbase = 0, craw = raw0;
   int b_cur = a.b;
   int seg_base = 0;
+  // WHOLE: sequences [s_begin, s_end), every group of each; the lens cache
+  // starts at s_begin
+  int s_begin = a.b, s_end = a.b;
+  if constexpr (WHOLE) {
+    const int wb = (int)gridDim.x < a.b ? (int)gridDim.x : a.b;
+    const int w = (int)blockIdx.x;
+    if (w < wb) {
+      s_begin = (int)((int64_t)a.b * w / wb);
+      s_end = (int)((int64_t)a.b * (w + 1) / wb);
+    }
+    b_cur = s_begin;
+    cbase = s_begin;
+    craw = (s_begin + lane < a.b) ? a.lens[s_begin + lane] : 0;
+  } else {
   if (t0 < t1 && nchunks == 1) {
     int u, u_incl;
     chunk_units(v0, incl0, u, u_incl);
@@ -599,7 +618,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 
 
-  if (nchunks != 1) sel.init(row, half);
+  }
+  if (WHOLE || nchunks != 1) sel.init(row, half);
   const size_t row_stride = (size_t)a.G * DH * sizeof(T);
   // lens entry of sequence bi (uniform), refilling the lane cache by chunks
   auto raw_of = [&](int bi) {
@@ -618,12 +638,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // at the end of the round, and nothing is stored while tiles still stream
   // (a wave's next loads would wait for those stores to complete).
   int t = t0;
+  int g_cur = 0;  // WHOLE: the next group of sequence b_cur
+  auto more = [&]() { return WHOLE ? b_cur < s_end : (t < t1 && b_cur < a.b); };
   bool first_round = true;
-  while (t < t1 && b_cur < a.b) {
+  while (more()) {
     // ---- the pieces of this round; lane p describes piece p ----
     int np = 0;
     int p_b = 0, p_g = 0, p_raw = 0, p_ta = 0, p_te = 0, p_nb = 0;
-    while (np < NW && t < t1 && b_cur < a.b) {
+    while (np < NW && more()) {
       const int raw = raw_of(b_cur);
       const SeqView sv = seq_view_raw(a, raw);
       const int nb = __builtin_amdgcn_readfirstlane((sv.L - sv.j0 + kTileRows - 1) / kTileRows);
@@ -632,25 +654,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         continue;
       }
       const int unit = nb + lead;  // units of one group of this sequence
-      const int g = a.G == 1 ? 0 : (t - seg_base) / unit;  // MQA: no division
+      const int g = WHOLE ? g_cur : a.G == 1 ? 0 : (t - seg_base) / unit;  // MQA: no division
       const int seg0 = seg_base + g * unit + lead;  // its first tile
       int ta, te;
       if constexpr (WHOLE) {
-        // whole segments: those whose first unit lies in [t0, t1)
-        if (seg0 - lead >= t1) {  // the next workgroup's
-          t = t1;
-          break;
-        }
         ta = 0;
         te = nb;
-        if (seg0 - lead < t0) {  // the previous workgroup's
-          t = seg0 + nb;
-          if (g == a.G - 1) {
-            seg_base += a.G * unit;
-            ++b_cur;
-          }
-          continue;
-        }
       } else {
         ta = (t > seg0 ? t : seg0) - seg0;
         te = (t1 < seg0 + nb ? t1 : seg0 + nb) - seg0;
@@ -669,7 +678,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       ++np;
       t = seg0 + te;
-      if (g == a.G - 1 && te == nb) {
+      if constexpr (WHOLE) {
+        if (++g_cur == a.G) {
+          g_cur = 0;
+          ++b_cur;
+        }
+      } else if (g == a.G - 1 && te == nb) {
         seg_base += a.G * unit;
         ++b_cur;
       }
@@ -905,7 +919,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
     }
     first_round = false;
-    if (t < t1 && b_cur < a.b) __syncthreads();  // the slots are reused
+    if (more()) __syncthreads();  // the slots are reused
+  }
+
+  if constexpr (WHOLE) {
+    // This workgroup's sequences: zeros for those with nothing visible, and
+    // after an append the lens bump (no other workgroup reads these entries,
+    // and this one has read them for the last time).  A full cache or a
+    // negative length keeps its lens and sets the error flag, as the combine
+    // does otherwise.
+    for (int c0 = s_begin + wave * 64; c0 < s_end; c0 += NW * 64) {
+      const int bi = c0 + lane;
+      const int raw = bi < s_end ? a.lens[bi] : 0;
+      uint64_t empty = __ballot(bi < s_end && tiles_of(seq_view_raw(a, raw)) == 0);
+      while (empty) {
+        const int be = c0 + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        T* op = reinterpret_cast<T*>(a.o) + (size_t)be * a.h * DH;
+        for (int e = lane; e < a.h * DH / 4; e += 64) store4(op + 4 * e, 0.f, 0.f, 0.f, 0.f);
+      }
+      if (a.k_new && bi < s_end) {
+        if (raw >= 0 && raw < a.m_cap)
+          a.lens[bi] = raw + 1;
+        else if (a.err_flag)
+          *a.err_flag = 1;
+      }
+    }
+    return;
   }
 
   // Workgroup 0 writes the schedule header for the combine and zeros the rows
@@ -1129,8 +1169,8 @@ constexpr int kDecodeWaves = 8;
 // heads of one segment.  Small blocks spread the records of a small step over
 // many CUs (a CU streams only ~20 GB/s).
 constexpr int kCombineThreads = 128;
-// Cache capacity (tiles) up to which a decode without an append takes every
-// segment whole (see launch_decode_t).
+// Cache capacity (tiles) up to which a decode takes whole sequences per
+// workgroup and skips the combine (see launch_decode_t).
 constexpr int kWholeMaxTiles = 8;
 
 // Workgroups of the decode launch for these shapes on the current device:
@@ -1196,13 +1236,12 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   a.window = p.window;
   a.rec_floats = (int)(decode_record_bytes(a.hg, DH) / sizeof(float));
   a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
-  // Short caches without an append: every segment goes whole to one
-  // workgroup (the one whose unit range holds its first unit; the ranges
-  // stay balanced to within one short segment), so no partial record is
-  // written and the combine is not launched.  (An append needs the combine
-  // for the lens bump, which must follow every workgroup's read of lens.)
-  const bool whole =
-      p.k_new == nullptr && (p.m_cap + kTileRows - 1) / kTileRows <= kWholeMaxTiles;
+  // Short caches: workgroup w takes sequences [b w / W, b (w + 1) / W) whole
+  // (every group), reading only their lens entries, so it writes no partial
+  // record and bumps their lens itself after an append: the combine is not
+  // launched.  (With longer caches, a count split would leave the work too
+  // uneven.)
+  const bool whole = (p.m_cap + kTileRows - 1) / kTileRows <= kWholeMaxTiles;
   hipError_t e;
   if (p.ev_begin && (e = hipEventRecord(p.ev_begin, s)) != hipSuccess) return e;
   if (whole)

@@ -79,47 +79,75 @@ def test_decode_parity_grid(case):
     assert_parity(o, ref, dtype, f"grid {case}")
 
 
-# Caches of at most 8 tiles, decoded without an append: every segment goes
-# whole to one workgroup, so the library writes no partial records (and does
-# not launch the combine).  The workspace is filled with a sentinel first; past
-# its schedule header ((b + 4) int32, padded to 256 bytes) it must still hold
-# it afterwards.
+# Caches of at most 8 tiles: every workgroup takes whole sequences, so the
+# library writes no partial records (and does not launch the combine; after an
+# append the decode kernel bumps lens itself).  The workspace is filled with a
+# sentinel first; past its schedule header ((b + 4) int32, padded to 256
+# bytes) it must still hold it afterwards.
 WHOLE_CASES = [
     # dtype, b, h, G, dh, m_cap, lens range
     (torch.bfloat16, 300, 32, 1, 128, 256, 0, 256),     # MQA, ragged, empty sequences
     (torch.bfloat16, 1024, 8, 1, 128, 128, 128, 128),   # the pages' setting (uniform lengths)
     (torch.bfloat16, 77, 16, 4, 64, 200, 1, 200),       # GQA, d_h 64
-    (torch.bfloat16, 2, 32, 32, 128, 64, 1, 64),        # MHA, fewer segments than workgroups
+    (torch.bfloat16, 2, 32, 32, 128, 64, 1, 64),        # MHA, fewer sequences than workgroups
     (torch.float32, 50, 8, 2, 128, 96, 0, 96),
 ]
 
 
+@pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("case", WHOLE_CASES, ids=lambda c: f"{str(c[0])[6:]}-b{c[1]}h{c[2]}G{c[3]}d{c[4]}m{c[5]}")
-def test_decode_short_caches_whole_segments(case):
+def test_decode_short_caches_whole_segments(case, append):
     dtype, b, h, G, dh, m_cap, lo, hi = case
-    announce(f"decode whole segments {case}")
-    cfg, inp = make(dtype, b, h, G, dh, m_cap, lo, hi, seed=7400 + b + h + G + dh)
+    announce(f"decode whole sequences {case} append={append}")
+    cfg, inp = make(dtype, b, h, G, dh, m_cap, lo, hi, seed=7400 + b + h + G + dh + append)
+    if append:
+        lens = inp["lens"].clone()
+        lens[::5] = m_cap  # full caches: no new row, lens kept, the flag set
+        inp["lens"] = lens
     d = to_dev(inp)
     ws = mqa.workspace_for(h, d["K"])
     ws.fill_(0xAB)
-    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if append:
+        o = mqa.append_decode(d["q"], d["k_new"], d["v_new"], d["K"], d["V"], d["lens"], cfg.scale,
+                              workspace=ws, err_flag=err)
+    else:
+        o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, workspace=ws)
     torch.cuda.synchronize()
-    ref, _ = oracle_step(inp, cfg.scale)
+    ref, lens_ref = oracle_step(inp, cfg.scale, append=append)
     assert_parity(o, ref, dtype, f"whole {case}")
+    assert d["lens"].cpu().tolist() == lens_ref.tolist()
     header = ((b + 4) * 4 + 255) // 256 * 256
     assert bool((ws[header:] == 0xAB).all()), "a partial record was written"
-    # a window over the same caches (still whole segments)
-    o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, window=17, workspace=ws)
-    torch.cuda.synchronize()
-    ref, _ = oracle_step(inp, cfg.scale, window=17)
-    assert_parity(o, ref, dtype, f"whole window {case}")
+    if append:
+        assert err.item() == 1
+        Kr, _ = oracle._raw(inp["K"])
+        Vr, _ = oracle._raw(inp["V"])
+        Kr, Vr = Kr.copy(), Vr.copy()
+        oracle.kv_append(inp["k_new"], inp["v_new"], Kr, Vr, inp["lens"].numpy().copy())
+        Kg, _ = oracle._raw(d["K"].cpu())
+        Vg, _ = oracle._raw(d["V"].cpu())
+        assert np.array_equal(Kg, Kr) and np.array_equal(Vg, Vr), "cache rows differ"
+    else:
+        # a window over the same caches
+        o = mqa.decode(d["q"], d["K"], d["V"], d["lens"], cfg.scale, window=17, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle_step(inp, cfg.scale, window=17)
+        assert_parity(o, ref, dtype, f"whole window {case}")
 
 
+# Caches of at most 8 tiles take whole sequences per workgroup; the schedule
+# tests below also run with m_cap just above that (the same lengths), so that
+# the split-K schedule's lens layouts stay covered.
+SPLIT_M = 300
+
+
+@pytest.mark.parametrize("m_cap", [96, SPLIT_M])
 @pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
-def test_decode_many_sequences_multi_chunk_scan(append, fused):
+def test_decode_many_sequences_multi_chunk_scan(append, fused, m_cap):
     """b > 64 exercises the multi-chunk wave scan of the schedule."""
-    announce(f"decode b=600 append={append} fused={fused}")
-    cfg, inp = make(torch.bfloat16, 600, 8, 1, 64, 96, 0, 95, seed=7100 + append)
+    announce(f"decode b=600 m_cap={m_cap} append={append} fused={fused}")
+    cfg, inp = make(torch.bfloat16, 600, 8, 1, 64, m_cap, 0, 95, seed=7100 + append)
     o, _ = run_decode(inp, cfg.scale, append=append, fused=fused)
     ref, _ = oracle_step(inp, cfg.scale, append=append)
     assert_parity(o, ref, torch.bfloat16, "b=600")
@@ -138,13 +166,14 @@ def test_decode_many_long_sequences_lead_in_schedule(append):
     assert_parity(o, ref, torch.bfloat16, "b=150 long")
 
 
+@pytest.mark.parametrize("m_cap", [64, SPLIT_M])
 @pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
-def test_decode_short_sequences_several_rounds(append, fused):
+def test_decode_short_sequences_several_rounds(append, fused, m_cap):
     """More segments than 8 per workgroup of the largest grid (256): some
     workgroup ranges cross more than NW = 8 segments, so they are streamed
     and folded in several rounds of at most 8 pieces."""
-    announce(f"decode b=4096 short append={append} fused={fused}")
-    cfg, inp = make(torch.bfloat16, 4096, 8, 1, 64, 64, 1, 40, seed=7300 + append)
+    announce(f"decode b=4096 short m_cap={m_cap} append={append} fused={fused}")
+    cfg, inp = make(torch.bfloat16, 4096, 8, 1, 64, m_cap, 1, 40, seed=7300 + append)
     assert cfg.b * cfg.G > 8 * 256
     o, _ = run_decode(inp, cfg.scale, append=append, fused=fused)
     ref, _ = oracle_step(inp, cfg.scale, append=append)
@@ -161,13 +190,14 @@ def test_decode_short_sequences_several_rounds_gqa_d128():
     assert_parity(o, ref, torch.float32, "b=1500 G=2 fp32 short")
 
 
+@pytest.mark.parametrize("m_cap", [48, SPLIT_M])
 @pytest.mark.parametrize("append,fused", [(False, True), (True, True), (True, False)])
-def test_decode_more_than_64_lens_chunks(append, fused):
+def test_decode_more_than_64_lens_chunks(append, fused, m_cap):
     """b = 5000 (79 chunks of 64 sequences): the schedule's general chunk walk,
     which refills the lens lane cache chunk by chunk; short ragged lengths
     with empty sequences."""
-    announce(f"decode b=5000 append={append} fused={fused}")
-    cfg, inp = make(torch.bfloat16, 5000, 8, 1, 64, 48, 0, 40, seed=7320 + 2 * append + fused)
+    announce(f"decode b=5000 m_cap={m_cap} append={append} fused={fused}")
+    cfg, inp = make(torch.bfloat16, 5000, 8, 1, 64, m_cap, 0, 40, seed=7320 + 2 * append + fused)
     assert (cfg.b + 63) // 64 > 64 and int((inp["lens"] == 0).sum()) > 0
     o, d = run_decode(inp, cfg.scale, append=append, fused=fused)
     ref, lens_ref = oracle_step(inp, cfg.scale, append=append)
@@ -175,14 +205,15 @@ def test_decode_more_than_64_lens_chunks(append, fused):
     assert d["lens"].cpu().numpy().tolist() == lens_ref.tolist()
 
 
+@pytest.mark.parametrize("m_cap", [100, SPLIT_M])
 @pytest.mark.parametrize("b", [65, 1024, 1025])
 @pytest.mark.parametrize("append", [False, True])
-def test_decode_lens_layout_boundaries(b, append):
+def test_decode_lens_layout_boundaries(b, append, m_cap):
     """Batch sizes at the edges of the schedule's lens layouts (one entry per
     lane up to 64, lane blocks of 16 up to 1024, chunks of 64 beyond), with
     empty rows mixed in and two groups."""
-    announce(f"decode layout boundary b={b} append={append}")
-    cfg, inp = make(torch.bfloat16, b, 8, 2, 64, 100, 0, 99, seed=7400 + b + append)
+    announce(f"decode layout boundary b={b} m_cap={m_cap} append={append}")
+    cfg, inp = make(torch.bfloat16, b, 8, 2, 64, m_cap, 0, 99, seed=7400 + b + append)
     lens = inp["lens"].clone()
     lens[::7] = 0  # rows with nothing visible (one visible row after an append)
     inp["lens"] = lens
