@@ -672,7 +672,7 @@ def main():
     log(f"decode kernel avg {kdur * 1e6:.2f} us, {achieved:.1f} GB/s")
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=measured_traffic(),
-                    kernel="decode_kernel<bf16,128,8>",
+                    kernel="decode_kernel<bf16,128,8,false>",
                     avg_launch_us=round(kdur * 1e6, 3),
                     algorithmic_bytes_per_launch=int(kbytes))
     del head
