@@ -509,6 +509,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // WHOLE: sequences [s_begin, s_end), every group of each; the lens cache
   // starts at s_begin
   int s_begin = a.b, s_end = a.b;
+  int raw_first = 0;  // lens entries s_begin .. s_begin + 63, as read at the start
   if constexpr (WHOLE) {
     const int wb = (int)gridDim.x < a.b ? (int)gridDim.x : a.b;
     const int w = (int)blockIdx.x;
@@ -519,6 +520,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     b_cur = s_begin;
     cbase = s_begin;
     craw = (s_begin + lane < a.b) ? a.lens[s_begin + lane] : 0;
+    raw_first = craw;
   } else {
   if (t0 < t1 && nchunks == 1) {
     int u, u_incl;
@@ -930,7 +932,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // does otherwise.
     for (int c0 = s_begin + wave * 64; c0 < s_end; c0 += NW * 64) {
       const int bi = c0 + lane;
-      const int raw = bi < s_end ? a.lens[bi] : 0;
+      // (the first 64 entries as read at the start: no second round trip)
+      const int raw = bi >= s_end ? 0 : c0 == s_begin ? raw_first : a.lens[bi];
       uint64_t empty = __ballot(bi < s_end && tiles_of(seq_view_raw(a, raw)) == 0);
       while (empty) {
         const int be = c0 + __builtin_ctzll(empty);
