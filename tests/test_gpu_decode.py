@@ -103,6 +103,7 @@ def test_decode_short_caches_whole_segments(case, append):
     if append:
         lens = inp["lens"].clone()
         lens[::5] = m_cap  # full caches: no new row, lens kept, the flag set
+        lens[1::11] = -3   # a negative length: no row either, nothing visible (zeros)
         inp["lens"] = lens
     d = to_dev(inp)
     ws = mqa.workspace_for(h, d["K"])
