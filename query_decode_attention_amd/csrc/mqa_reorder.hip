@@ -41,6 +41,14 @@ __global__ __launch_bounds__(256) void reorder_rows_kernel(ReorderParams p) {
   const size_t off = (size_t)pos * p.row_bytes + (size_t)c * 16;
   for (int grp = blockIdx.y; grp < groups; grp += gridDim.y) {
     const int base = grp * p.beam;
+    // The group's parents and lengths, loaded together (one round trip
+    // before the copy's loads, not a parent load and then a length load).
+    int par[MB], lg[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      par[i] = i < p.beam ? p.parent[base + i] : i;
+      lg[i] = i < p.beam ? p.lens[base + i] : 0;
+    }
     // Which rows move, where from, and how many positions (uniform).
     int src[MB], len[MB];
     int span = 0;
@@ -49,10 +57,13 @@ __global__ __launch_bounds__(256) void reorder_rows_kernel(ReorderParams p) {
       src[i] = i;
       len[i] = 0;
       if (i < p.beam) {
-        const int par = p.parent[base + i];
-        if (par >= 0 && par < p.beam) {
-          src[i] = par;
-          if (par != i) len[i] = clamp_len(p.lens[base + par], p.m_cap);
+        if (par[i] >= 0 && par[i] < p.beam) {
+          src[i] = par[i];
+          int L = lg[0];
+#pragma unroll
+          for (int k = 1; k < MB; ++k)
+            if (par[i] == k) L = lg[k];  // par[i] is uniform: a scalar choice
+          if (par[i] != i) len[i] = clamp_len(L, p.m_cap);
         } else if (blockIdx.x == 0 && threadIdx.x == 0 && p.err_flag) {
           *p.err_flag = 1;
         }
@@ -63,31 +74,35 @@ __global__ __launch_bounds__(256) void reorder_rows_kernel(ReorderParams p) {
     }
     if (p.lens_out && blockIdx.x == 0 && (int)threadIdx.x < p.beam) {
       const int i = base + (int)threadIdx.x;
-      const int par = p.parent[i];
-      p.lens_out[i] = (par >= 0 && par < p.beam) ? p.lens[base + par] : p.lens[i];
+      const int pr = p.parent[i];
+      p.lens_out[i] = (pr >= 0 && pr < p.beam) ? p.lens[base + pr] : p.lens[i];
     }
     if (pos >= span) continue;
-    for (int half = 0; half < 2; ++half) {
-      char* at = (half == 0 ? p.k : p.v) + (size_t)base * seq + off;
-      // every source chunk first, then the moved rows: in place is safe
-      u32x4 x[MB];
+    // Every source chunk, K and V, is loaded before any moved row is stored:
+    // in place is safe, and the K and V loads are in flight together.
+    char* at[2] = {p.k + (size_t)base * seq + off, p.v + (size_t)base * seq + off};
+    u32x4 x[2][MB];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int s = 0; s < MB; ++s) {
         bool need = false;
 #pragma unroll
         for (int i = 0; i < MB; ++i) need |= (src[i] == s && src[i] != i && pos < len[i]);
-        x[s] = need ? *reinterpret_cast<const u32x4*>(at + (size_t)s * seq) : u32x4{0u, 0u, 0u, 0u};
+        x[half][s] = need ? *reinterpret_cast<const u32x4*>(at[half] + (size_t)s * seq)
+                          : u32x4{0u, 0u, 0u, 0u};
       }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         if (src[i] == i || pos >= len[i]) continue;
-        u32x4 v = x[0];
+        u32x4 v = x[half][0];
 #pragma unroll
         for (int s = 1; s < MB; ++s)
-          if (src[i] == s) v = x[s];  // src[i] is uniform: a scalar choice
-        *reinterpret_cast<u32x4*>(at + (size_t)i * seq) = v;
+          if (src[i] == s) v = x[half][s];  // src[i] is uniform: a scalar choice
+        *reinterpret_cast<u32x4*>(at[half] + (size_t)i * seq) = v;
       }
-    }
   }
 }
 
