@@ -42,10 +42,17 @@
 // wide) copies it into the wave's own fold slot (free until the wave parks)
 // and reads it chunk by chunk.
 //
+// Whole sequences.  When every cache holds at most kWholeMaxTiles tiles, the
+// kernel is instantiated with WHOLE: workgroup w takes whole sequences (all
+// their groups), reads only its own lens entries, finishes every segment
+// itself and writes no partial record, so no combine kernel runs.
+//
 // Fused append.  With k_new/v_new, sequence b attends over L_old + 1
 // positions; the row at L_old is read from k_new/v_new (never from the cache)
 // and the wave that owns it stores it into the cache.  lens itself is bumped
-// by the combine kernel, after every decode workgroup has read it.
+// by the combine kernel, after every decode workgroup has read it (with
+// WHOLE, by the workgroup that owns the sequence, at its end: no other
+// workgroup reads that entry).
 //
 // One wave, one 32-position tile, all h/G <= 32 heads of the group:
 //   S^T[32 pos][32 heads] = K_tile . Q^T        (MFMA; K rows are the A operand
@@ -97,7 +104,7 @@ struct DecodeArgs {
   const char* q;
   char* k;               // cache; written only at the appended row
   char* v;
-  int32_t* lens;         // read; +1 at the end of the kernel when appending
+  int32_t* lens;         // read; with WHOLE and an append, +1 at the workgroup's end
   const char* k_new;     // nullable: no fused append
   const char* v_new;
   int32_t* err_flag;     // nullable

@@ -45,15 +45,11 @@ struct PrefillArgs {
 // MASK (non-causal only): kMaskNone, kMaskKeys (one value per key: the
 // head and query strides are 0, as for key padding) or kMaskFull.
 constexpr int kMaskNone = 0, kMaskKeys = 1, kMaskFull = 2;
-// (Not inlined: the bf16 kernel calls it only to recompute a workgroup whose
-// logits outgrew their fixed softmax reference, and inlining it there would
-// add its registers to the bf16 kernel's hot loops.)
-//
-// Its LDS comes from the caller: the fp32 kernel's own arrays, or, in the
-// bf16 kernel's rescue, the bf16 loops' tile buffers (free by then).
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_float;
+// LDS bytes prefill_rows uses (double-buffered K chunks, transposed V
+// chunks and the per-key mask of a tile).
 template <typename T, int DH>
 struct RowsLds {
   using S = TileShape<T, DH>;
@@ -61,6 +57,14 @@ struct RowsLds {
   static constexpr size_t kBytesVt = 2 * S::ND * S::VTC * 64 * sizeof(u32x4);    // s_vt[2][ND][VTC][64]
   static constexpr size_t kBytesKb = 2 * (kTileRows / 4) * sizeof(f32x4);        // s_kb[2][8]
 };
+
+// The rescaling body: the workgroup's rows with a running softmax maximum
+// (the fp32 kernel, and the bf16 kernel's rescue).  Not inlined: the bf16
+// kernel calls it only to recompute a workgroup whose logits outgrew their
+// fixed softmax reference, and inlining it there would add its registers to
+// the bf16 kernel's hot loops.  Its LDS comes from the caller: the fp32
+// kernel's own arrays, or, in the bf16 kernel's rescue, the bf16 loops' tile
+// buffers (free by then).
 template <typename T, int DH, int NW, bool CAUSAL, bool FOLD, int MASK>
 __device__ __attribute__((noinline)) void prefill_rows(const PrefillArgs a, lds_u32x4* k_mem,
                                                        lds_u32x4* vt_mem, lds_f32x4* kb_mem) {
