@@ -187,3 +187,55 @@ def test_beam_steps_ping_pong_lens(dtype):
     assert int(flag.item()) == 0
     assert raw(d["K"].cpu()).tobytes() == Kr.tobytes()
     assert raw(d["V"].cpu()).tobytes() == Vr.tobytes()
+
+
+def _reorder_sweep_cases(n_cases, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        beam = int(rng.choice([1, 2, 3, 4, 4, 5, 8, 12, 16]))
+        groups = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 1, 2, 4, 8]))
+        dh = int(rng.choice([64, 128]))
+        m_cap = int(rng.choice([1, 5, 31, 32, 33, 100, 257]))
+        out_of_place = bool(rng.random() < 0.5)
+        cases.append((i, dtype, groups * beam, beam, G, dh, m_cap, out_of_place,
+                      int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+REORDER_SWEEP = _reorder_sweep_cases(32, 20261206)
+
+
+@pytest.mark.parametrize("case", REORDER_SWEEP,
+                         ids=lambda c: f"{c[0]:02d}-{c[1]}-b{c[2]}beam{c[3]}G{c[4]}d{c[5]}m{c[6]}"
+                                       + ("-to" if c[7] else ""))
+def test_reorder_sweep_bit_exact(case):
+    """Seeded random reorders: beam widths 1..16, groups, head sizes and
+    capacities, lengths drawn past both ends of [0, m_cap], a few bad
+    parents; in place or with the lengths written to a second array.  The
+    whole cache must equal the oracle's byte for byte, the lengths exactly."""
+    i, dt, b, beam, G, dh, m_cap, out_of_place, seed = case
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    what = f"reorder sweep {case}"
+    announce(what)
+    K, V, g = cache(dtype, b, m_cap, G, dh, seed)
+    lens = torch.randint(-2, m_cap + 4, (b,), generator=g, dtype=torch.int32)
+    parent = torch.randint(0, beam, (b,), generator=g, dtype=torch.int32)
+    bad = torch.rand(b, generator=g) < 0.05
+    parent[bad] = beam + 1
+    dK, dV, dl, dp = K.cuda(), V.cuda(), lens.cuda(), parent.cuda()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lo = torch.full((b,), -7, dtype=torch.int32, device="cuda") if out_of_place else None
+    mqa.kv_reorder(dK, dV, dl, dp, beam, err_flag=flag, lens_out=lo)
+    torch.cuda.synchronize()
+    Kr, Vr, lr = raw(K), raw(V), lens.numpy().copy()
+    oracle_bad = oracle.kv_reorder(Kr, Vr, lr, parent.numpy(), beam)
+    got_lens = (lo if out_of_place else dl).cpu().numpy()
+    assert np.array_equal(got_lens, lr), what
+    if out_of_place:
+        assert torch.equal(dl.cpu(), lens), what + ": lens_in changed"
+    assert raw(dK.cpu()).tobytes() == Kr.tobytes(), what + ": K"
+    assert raw(dV.cpu()).tobytes() == Vr.tobytes(), what + ": V"
+    assert int(flag.item()) == (1 if oracle_bad else 0), what + ": flag"

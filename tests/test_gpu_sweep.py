@@ -23,7 +23,13 @@ if torch.cuda.is_available():
 MIXES = ("uniform", "short_long", "with_empty", "constant", "one_long", "full")
 
 
-def _draw_cases(n, seed):
+CAPS = (1, 31, 32, 33, 96, 257, 600, 1500, 4000)
+# around the capacity up to which a decode keeps every sequence whole in one
+# workgroup (8 tiles of 32 positions) and runs no merge
+CAPS_WHOLE_EDGE = (200, 224, 255, 256, 257, 288)
+
+
+def _draw_cases(n, seed, caps=CAPS, first=0):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -32,7 +38,7 @@ def _draw_cases(n, seed):
         G = int(rng.choice([1, 1, 2, 4, 8]))
         hg = int(rng.choice([1, 2, 3, 5, 8, 16, 24, 32]))
         b = int(rng.choice([1, 2, 7, 33, 64, 65, 130, 300, 700, 2100]))
-        m_cap = int(rng.choice([1, 31, 32, 33, 96, 257, 600, 1500, 4000]))
+        m_cap = int(rng.choice(caps))
         mix = str(rng.choice(MIXES))
         append = bool(rng.random() < 0.5)
         if append and mix == "full":
@@ -43,12 +49,12 @@ def _draw_cases(n, seed):
         # keep the oracle to seconds and the caches to a few hundred MB
         while b > 1 and (b * m_cap * G * dh > 40_000_000 or b * hg * G * m_cap * dh > 300_000_000):
             b = max(1, b // 3)
-        cases.append((len(cases), dtype, b, hg * G, G, dh, m_cap, mix, append, fused, window,
+        cases.append((first + len(cases), dtype, b, hg * G, G, dh, m_cap, mix, append, fused, window,
                       scale_mult, int(rng.integers(1, 1 << 30))))
     return cases
 
 
-CASES = _draw_cases(64, 20261203)
+CASES = _draw_cases(64, 20261203) + _draw_cases(24, 20261207, CAPS_WHOLE_EDGE, first=64)
 
 
 def _lens(mix, b, m_cap, append, gen):
